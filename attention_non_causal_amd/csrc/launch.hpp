@@ -1,0 +1,39 @@
+// launch.hpp -- internal launchers behind the C ABI (not part of the public
+// header).  Arguments are validated by the caller (api.cpp) before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace dit {
+
+struct FwdArgs {
+    const void* q;         // bf16 [B][Sq][H][d]  or e4m3 bytes for the fp8 path
+    const void* k;         // bf16 [B][Skv][H][d] or e4m3
+    const void* v;         // bf16 [B][Skv][H][d] or e4m3
+    const float* q_scale;  // fp8 path: fp32 [B][H][ceil(Sq/128)]
+    const float* k_scale;  // fp8 path: fp32 [B][H][ceil(Skv/128)]
+    const float* v_scale;  // fp8 path: fp32 [B][H][ceil(Skv/128)]
+    void* o;               // bf16 [B][Sq][H][d]
+    float* lse;            // fp32 [B][H][Sq]
+    int B, H, Sq, Skv, d;
+    float scale;
+};
+
+constexpr int kMaxMergeParts = 16;
+
+struct MergeArgs {
+    const void* o_parts[kMaxMergeParts];
+    const float* lse_parts[kMaxMergeParts];
+    int n_parts;
+    void* o;
+    float* lse;
+    int B, H, Sq, d;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_quant_fp8(const void* x, void* x8, float* scale, int B, int H, int S, int d,
+                            hipStream_t stream);
+
+}  // namespace dit

@@ -1,0 +1,112 @@
+"""torch-facing helpers: allocate outputs with torch and call the C ABI.
+
+Marshalling only -- the computation is the library's HIP kernels.  Tensors
+are contiguous [B, S, H, d] on a ROCm device; LSE is fp32 [B, H, Sq].
+"""
+from __future__ import annotations
+
+import math
+
+from . import _lib
+
+
+def _require(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B,S,H,d]")
+
+
+def attention(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
+    """bf16 non-causal attention: returns (o bf16 [B,Sq,H,d], lse fp32 [B,H,Sq])."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, torch.bfloat16, n)
+    B, Sq, H, d = q.shape
+    Skv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _lib.dit_attn_fwd(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16, stream)
+    return out, lse
+
+
+def quantize_fp8(x, stream=None):
+    """Per-(b, h, 128-token) e4m3 quantisation: returns (x8 uint8 [B,S,H,d],
+    scale fp32 [B,H,ceil(S/128)])."""
+    import torch
+    _require(x, torch.bfloat16, "x")
+    B, S, H, d = x.shape
+    x8 = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
+    nblk = (S + _lib.DIT_FP8_BLOCK - 1) // _lib.DIT_FP8_BLOCK
+    sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    _lib.dit_quant_fp8(x, x8, sc, B, H, S, d, stream)
+    return x8, sc
+
+
+def attention_fp8(q8, q_scale, k8, k_scale, v8, v_scale, scale: float | None = None,
+                  out=None, lse=None, stream=None):
+    """fp8 (e4m3) non-causal attention on quantised inputs from quantize_fp8."""
+    import torch
+    B, Sq, H, d = q8.shape
+    Skv = k8.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
+    dq = _lib.fp8_tensor(q8, q_scale)
+    dk = _lib.fp8_tensor(k8, k_scale)
+    dv = _lib.fp8_tensor(v8, v_scale)
+    _lib.dit_attn_fwd(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_FP8_E4M3,
+                      stream)
+    return out, lse
+
+
+def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """LSE-merge of partial results (lists of bf16 [B,Sq,H,d] / fp32 [B,H,Sq])."""
+    import torch
+    B, Sq, H, d = o_parts[0].shape
+    if out is None:
+        out = torch.empty_like(o_parts[0])
+    if lse is None:
+        lse = torch.empty_like(lse_parts[0])
+    _lib.dit_attn_merge(o_parts, lse_parts, len(o_parts), out, lse, B, H, Sq, d, stream)
+    return out, lse
+
+
+def ring_share_attention(q, k, v, n_chunks: int, scale: float | None = None, parts=None,
+                         out=None, lse=None, stream=None):
+    """One ring rank's share of ring attention, run locally: the local queries
+    attend to each of ``n_chunks`` consecutive KV chunks (one forward launch
+    each, on pointer offsets into k/v, so B must be 1), then the partials are
+    merged.  ``parts`` = optional preallocated (o_parts, lse_parts) lists."""
+    import torch
+    B, Sq, H, d = q.shape
+    Skv = k.shape[1]
+    if B != 1:
+        raise ValueError("KV chunks are pointer offsets: B must be 1")
+    if Skv % n_chunks:
+        raise ValueError("Skv must be a multiple of n_chunks")
+    c = Skv // n_chunks
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if parts is None:
+        o_parts = [torch.empty_like(q) for _ in range(n_chunks)]
+        lse_parts = [torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+                     for _ in range(n_chunks)]
+    else:
+        o_parts, lse_parts = parts
+    es = k.element_size()
+    for i in range(n_chunks):
+        off = i * c * H * d * es
+        _lib.dit_attn_fwd(q, k.data_ptr() + off, v.data_ptr() + off, o_parts[i], lse_parts[i],
+                          B, H, Sq, c, d, scale, _lib.DIT_DTYPE_BF16, stream)
+    return merge(o_parts, lse_parts, out, lse, stream)

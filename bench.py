@@ -1,0 +1,217 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+Headline: attention TFLOP/s (4*B*H*Sq*Skv*d / time) of the bf16 forward pass on
+the FLUX-like workload (B1 H24 S16896 d128), with inputs already resident in
+HBM.  A step is one dit_attn_fwd launch over the whole workload.  The kernel's
+average launch duration is measured with HIP events on the stream it runs on,
+and compared with MI355X's dense bf16 MFMA peak (2.5 PFLOP/s).  The fp64 CPU
+oracle is timed on a bounded sample of the same workload (cpu_baseline).
+
+Extra lines of the hot path (fp8 forward with its quantiser, the SD3-like and
+tiny shapes, and one ring rank's share: four chunk forwards + the LSE-merge) are
+timed the same way and reported under "extras".
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_launches(fn, steps, warmup):
+    """Run fn() warmup times, then time `steps` calls: returns (wall ms per call
+    between two synchronisations, list of per-call event ms on torch's current
+    stream, which is the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_baseline(W, g, budget_s):
+    """Time the fp64 oracle on a bounded sample of query rows (all heads, all
+    keys) of the same workload; report its TFLOP/s."""
+    import oracle
+    from attention_non_causal_amd import workloads as wl
+    t0 = time.perf_counter()
+    oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=[0])
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(W.Sq, budget_s / max(t1, 1e-3))))
+    rows = wl.sample_rows(W.Sq, n)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * W.B * W.H * len(rows) * W.Skv * W.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {W.Sq} query rows x all {W.H} heads x {W.Skv} keys "
+                      f"(d{W.d}, fp64) in {dt:.1f} s"}
+
+
+def bench_fwd(W, g, dev, steps, warmup):
+    import torch
+    from attention_non_causal_amd import functional as F
+    q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((W.B, W.H, W.Sq), dtype=torch.float32, device=dev)
+    wall, evs = time_launches(lambda: F.attention(q, k, v, W.scale, out=o, lse=lse), steps,
+                              warmup)
+    return wall, evs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for cpu_baseline (0: skip)")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design, not a build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from attention_non_causal_amd import workloads as wl
+    from attention_non_causal_amd import functional as F
+
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    W = wl.WORKLOADS[args.workload]
+    log(f"{props.name}: {props.multi_processor_count} CUs; workload {W.name}: generating inputs")
+    g = wl.generate(W)
+    wall, evs = bench_fwd(W, g, dev, args.steps, args.warmup)
+    kern_ms = float(np.mean(evs))
+    value = W.flops / (wall * 1e-3) / 1e12
+    achieved = W.flops / (kern_ms * 1e-3) / 1e12
+    log(f"fwd {W.name}: wall {wall:.3f} ms/step, event mean {kern_ms:.3f} ms "
+        f"(min {min(evs):.3f}) -> {achieved:.1f} TFLOP/s")
+
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(dev, max(3, args.steps // 4), 2)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log("cpu_baseline: timing the oracle on a row sample")
+        cpu = cpu_baseline(W, g, args.cpu_budget)
+        log(f"cpu_baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "attention TFLOP/s & % of MFMA peak, B1 H24 S=16896 d128 bf16",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), Q/K RMS-normalised), no dataset or weights",
+        "config": {"workload": W.description, "B": W.B, "H": W.H, "Sq": W.Sq, "Skv": W.Skv,
+                   "d": W.d, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "fwd_bf16_kernel<128>",
+                     "kernel_ms": round(kern_ms, 4)},
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "extras": extras,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_extras(dev, steps, warmup):
+    import numpy as np
+    import torch
+    from attention_non_causal_amd import _lib, functional as F
+    from attention_non_causal_amd import workloads as wl
+    res = {}
+    for name in ("tiny", "sd3"):
+        W = wl.WORKLOADS[name]
+        g = wl.generate(W)
+        wall, evs = bench_fwd(W, g, dev, steps, warmup)
+        ms = float(np.mean(evs))
+        res[name] = {"kernel_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1)}
+        log(f"extra {name}: {ms:.3f} ms, {res[name]['tflops']} TFLOP/s")
+
+    W = wl.WORKLOADS["wan_ring"]
+    g = wl.generate(W)
+    q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)
+    del g
+    parts = ([torch.empty_like(q) for _ in range(W.n_chunks)],
+             [torch.empty((1, W.H, W.Sq), dtype=torch.float32, device=dev)
+              for _ in range(W.n_chunks)])
+    o = torch.empty_like(q)
+    lse = torch.empty((1, W.H, W.Sq), dtype=torch.float32, device=dev)
+    wall, evs = time_launches(
+        lambda: F.ring_share_attention(q, k, v, W.n_chunks, W.scale, parts=parts, out=o, lse=lse),
+        steps, warmup)
+    ms = float(np.mean(evs))
+    _, mevs = time_launches(lambda: F.merge(parts[0], parts[1], out=o, lse=lse), steps, warmup)
+    mms = float(np.mean(mevs))
+    merge_bytes = W.n_chunks * (W.Sq * W.H * W.d * 2 + W.H * W.Sq * 4) + W.Sq * W.H * W.d * 2 \
+        + W.H * W.Sq * 4
+    res["wan_ring"] = {"total_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1),
+                       "merge_ms": round(mms, 4),
+                       "merge_GBs": round(merge_bytes / mms / 1e6, 1)}
+    log(f"extra wan_ring: {ms:.3f} ms total ({res['wan_ring']['tflops']} TFLOP/s), merge "
+        f"{mms:.3f} ms = {res['wan_ring']['merge_GBs']} GB/s")
+    del q, k, v, parts, o, lse
+
+    W = wl.WORKLOADS["flux_fp8"]
+    g = wl.generate(W)
+    x = to_dev(g["k"], dev)
+    x8 = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    sc = torch.empty((W.B, W.H, (W.Skv + 127) // 128), dtype=torch.float32, device=dev)
+    _, qevs = time_launches(lambda: _lib.dit_quant_fp8(x, x8, sc, W.B, W.H, W.Skv, W.d), steps,
+                            warmup)
+    qms = float(np.mean(qevs))
+    qbytes = W.B * W.Skv * W.H * W.d * 3 + sc.numel() * 4
+    res["quant_fp8"] = {"kernel_ms": round(qms, 4), "GBs": round(qbytes / qms / 1e6, 1)}
+    log(f"extra quant_fp8 (one tensor): {qms:.4f} ms = {res['quant_fp8']['GBs']} GB/s")
+    return res
+
+
+if __name__ == "__main__":
+    main()

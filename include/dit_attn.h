@@ -1,0 +1,145 @@
+/*
+ * dit_attn.h -- C ABI of the MI355X (gfx950) non-causal attention library for
+ * DiT inference: the attention forward pass (O and log-sum-exp), the
+ * log-sum-exp merge of partial results over KV chunks, and the
+ * per-(head, 128-token block) e4m3 quantiser that feeds the fp8 forward pass.
+ *
+ * Where the operations come from
+ *   "xDiT 项目概述" (intelliparadigm.com), sec. 2.1: DiT inference runs the
+ *   whole token sequence at once (prefill-like, compute-bound), with no KV
+ *   cache and no paging -- so attention here is dense, non-causal and takes
+ *   contiguous Q/K/V.  Sec. 2.2: sequences are long (tens of thousands of
+ *   joint text+image/video tokens).  Sec. 3.2 (USP): the ring dimension splits
+ *   the sequence into blocks that travel around a ring of GPUs; one GPU's
+ *   share is its queries against one KV block at a time, and the partial
+ *   results are combined -- dit_attn_merge is that combination.
+ *   "AMD、Radeon AI PRO R9700S最大4台で..." (aisoku.org), tuning section and
+ *   quick-start flags: attention runs through a dedicated FP8 attention
+ *   backend; FP8 changes outputs, so it is checked against fixed seeds.
+ *   "生成AI推論を速くするための設計ノート" sec. 3: a block-scaled low-precision
+ *   tensor is a payload plus per-block scales; sec. 5: a dedicated kernel for
+ *   an op whose structure a general one does not fit; sec. 4: launches with no
+ *   host sync or allocation can be captured into a graph.
+ *
+ * The attention formula is never printed on those pages; this library computes
+ * the plain reading, per batch b and head h:
+ *     S   = scale * Q K^T                  (no mask, no bias: non-causal)
+ *     O   = softmax_rows(S) V
+ *     LSE = ln sum_j exp(S_ij)             (natural log, scale included)
+ *
+ * Conventions shared by every entry point
+ *   Layouts: Q, O [B][Sq][H][d]; K, V [B][Skv][H][d]; all contiguous with d
+ *   fastest.  LSE [B][H][Sq] fp32.  bf16 is IEEE bfloat16 bits; e4m3 is OCP
+ *   E4M3FN (bias 7, max 448, no infinities).
+ *   Ownership: the caller owns every buffer.  The library allocates nothing,
+ *   keeps no state between calls, never synchronises, and only enqueues work
+ *   on `stream` (0 = the null stream), so every call can be captured into a
+ *   HIP graph.  Calls are thread-safe.
+ *   Errors: every argument is validated on the host before any HIP call, so an
+ *   invalid call returns its status code without touching the device.  A
+ *   launch failure returns DIT_ERR_HIP.  Faults inside a kernel surface, as
+ *   for any asynchronous HIP work, at the caller's next synchronisation.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_ATTN_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+enum dit_status {
+    DIT_OK = 0,
+    DIT_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    DIT_ERR_SHAPE = 2,       /* B, H, Sq, Skv or S < 1, or a size overflows 2^62 B  */
+    DIT_ERR_UNSUPPORTED = 3, /* d not 64/128, unknown dtype, n_parts not in 1..16   */
+    DIT_ERR_ALIGN = 4,       /* tensor not 16-byte aligned (LSE/scales: 4-byte)    */
+    DIT_ERR_VALUE = 5,       /* scale not finite or not > 0                        */
+    DIT_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap     */
+    DIT_ERR_HIP = 7          /* the HIP launch reported an error                   */
+};
+
+enum dit_dtype {
+    DIT_DTYPE_BF16 = 0,
+    DIT_DTYPE_FP8_E4M3 = 1
+};
+
+/* Block size (tokens) of the e4m3 per-(b, h, block) scales. */
+#define DIT_FP8_BLOCK 128
+
+/* An e4m3 tensor with its block scales, as produced by dit_quant_fp8.
+ *   data : device, e4m3 bytes [B][S][H][d]
+ *   scale: device, fp32 [B][H][ceil(S/128)]; x[b,s,h,c] ~= e4m3(data) * scale[b,h,s/128]
+ * The descriptor itself lives in host memory and is read during the call only. */
+typedef struct dit_fp8_tensor {
+    const void* data;
+    const float* scale;
+} dit_fp8_tensor_t;
+
+/*
+ * dit_attn_fwd -- non-causal attention forward pass, O and LSE.
+ *
+ *   dtype == DIT_DTYPE_BF16:     q, k, v are device pointers to bf16 tensors.
+ *   dtype == DIT_DTYPE_FP8_E4M3: q, k, v each point to a HOST dit_fp8_tensor_t
+ *       describing an e4m3 tensor and its block scales.  Q.K^T and P.V run on
+ *       fp8 MFMA with fp32 accumulation; the block scales are applied inside
+ *       the kernel; P is rounded to e4m3 (relative to the running row maximum)
+ *       before P.V and the row sum uses the same rounded values.
+ *   o:   device, bf16 [B][Sq][H][d] (fp32 result rounded to nearest even).
+ *   lse: device, fp32 [B][H][Sq].
+ *   d:   64 or 128.  Sq, Skv >= 1 (any value: tails are masked).
+ *   scale: the softmax scale (e.g. 1/sqrt(d)), finite and > 0; used as given.
+ *   o and lse must not overlap q, k, v or each other (DIT_ERR_ALIAS).
+ */
+int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Sq, int Skv, int d, float scale, int dtype,
+                 hipStream_t stream);
+
+/*
+ * dit_attn_merge -- combine n partial attention results over disjoint key
+ * blocks into the result over their union, per (b, s, h) row:
+ *     M   = max_c LSE_c
+ *     w_c = exp(LSE_c - M)
+ *     O   = sum_c w_c O_c / sum_c w_c,     LSE = M + ln sum_c w_c
+ * A part whose LSE is -inf has weight 0; if every part is -inf the row gets
+ * O = 0 and LSE = -inf.  Accumulation is fp32.
+ *
+ *   o_parts, lse_parts: HOST arrays of n_parts device pointers to bf16
+ *       [B][Sq][H][d] partial outputs and fp32 [B][H][Sq] partial LSEs
+ *       (exactly what dit_attn_fwd writes).
+ *   n_parts: 1..16.
+ *   o, lse: device outputs in the same layouts.  o may be exactly o_parts[0]
+ *       and lse exactly lse_parts[0] (in-place merge); any other overlap of an
+ *       output with an input returns DIT_ERR_ALIAS.
+ */
+int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, int n_parts,
+                   void* o, float* lse, int B, int H, int Sq, int d, hipStream_t stream);
+
+/*
+ * dit_quant_fp8 -- per-(b, h, 128-token block) e4m3 quantisation of a bf16
+ * tensor [B][S][H][d].  For each block (the last one may hold S mod 128 tokens):
+ *     amax  = max |x| over the block's tokens and all d channels
+ *     inv   = fp32(448 / amax),  x8 = e4m3_rne(fp32(x * inv))
+ *     scale = fp32(amax / 448)                   (amax == 0: scale 1, x8 = 0)
+ * Every fp32 step is a single correctly rounded operation, so the output is
+ * bit-reproducible.
+ *   x: device bf16 [B][S][H][d];  x_fp8: device e4m3 [B][S][H][d];
+ *   scale: device fp32 [B][H][ceil(S/128)].  Outputs must not overlap x.
+ */
+int dit_quant_fp8(const void* x, void* x_fp8, float* scale, int B, int H, int S, int d,
+                  hipStream_t stream);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* dit_status_string(int status);
+
+/* DIT_ATTN_VERSION of the built library. */
+int dit_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

@@ -1,0 +1,141 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+the public header declares, and rejects every invalid argument with its status
+code before any HIP call (fake, never-dereferenced device addresses are used;
+no call here reaches a kernel launch)."""
+import ctypes
+import math
+import subprocess
+
+import pytest
+
+from attention_non_causal_amd import _lib
+from attention_non_causal_amd._lib import (DIT_DTYPE_BF16, DIT_DTYPE_FP8_E4M3, DIT_ERR_ALIAS,
+                                           DIT_ERR_ALIGN, DIT_ERR_NULL, DIT_ERR_SHAPE,
+                                           DIT_ERR_UNSUPPORTED, DIT_ERR_VALUE)
+
+G = 1 << 40  # fake device addresses, 1 TiB apart: never overlap by accident
+Q, K, V, O, L = 1 * G, 2 * G, 3 * G, 4 * G, 5 * G
+
+
+def fwd(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
+        dtype=DIT_DTYPE_BF16):
+    return _lib.dit_attn_fwd_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, stream=0)
+
+
+def test_library_exports_header_functions():
+    names = _lib.header_functions()
+    assert set(names) == {"dit_attn_fwd", "dit_attn_merge", "dit_quant_fp8",
+                          "dit_status_string", "dit_version"}
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert _lib.dit_version() == 10000
+    texts = [_lib.dit_status_string(s) for s in range(8)]
+    assert len(set(texts)) == 8 and all(texts)
+    assert _lib.dit_status_string(99) == "unknown status"
+    assert _lib.dit_status_string(-1) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), DIT_ERR_NULL), (dict(k=None), DIT_ERR_NULL), (dict(v=None), DIT_ERR_NULL),
+    (dict(o=None), DIT_ERR_NULL), (dict(lse=None), DIT_ERR_NULL),
+    (dict(dtype=2), DIT_ERR_UNSUPPORTED), (dict(dtype=-1), DIT_ERR_UNSUPPORTED),
+    (dict(d=96), DIT_ERR_UNSUPPORTED), (dict(d=256), DIT_ERR_UNSUPPORTED),
+    (dict(d=0), DIT_ERR_UNSUPPORTED),
+    (dict(B=0), DIT_ERR_SHAPE), (dict(H=0), DIT_ERR_SHAPE), (dict(Sq=0), DIT_ERR_SHAPE),
+    (dict(Skv=0), DIT_ERR_SHAPE), (dict(Skv=-5), DIT_ERR_SHAPE),
+    (dict(B=1 << 30, H=1 << 30, Sq=1 << 30), DIT_ERR_SHAPE),
+    (dict(scale=0.0), DIT_ERR_VALUE), (dict(scale=-0.125), DIT_ERR_VALUE),
+    (dict(scale=math.inf), DIT_ERR_VALUE), (dict(scale=math.nan), DIT_ERR_VALUE),
+    (dict(q=Q + 8), DIT_ERR_ALIGN), (dict(k=K + 2), DIT_ERR_ALIGN), (dict(v=V + 4), DIT_ERR_ALIGN),
+    (dict(o=O + 8), DIT_ERR_ALIGN), (dict(lse=L + 2), DIT_ERR_ALIGN),
+    (dict(o=Q + 4096), DIT_ERR_ALIAS), (dict(o=V - 16), DIT_ERR_ALIAS),
+    (dict(lse=K + 64), DIT_ERR_ALIAS), (dict(lse=O + 1024), DIT_ERR_ALIAS),
+])
+def test_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_fwd_fp8_descriptor_checks():
+    good = [_lib.fp8_tensor(Q, Q + (1 << 30)), _lib.fp8_tensor(K, K + (1 << 30)),
+            _lib.fp8_tensor(V, V + (1 << 30))]
+    bad_data = _lib.fp8_tensor(None, Q + (1 << 30))
+    bad_scale = _lib.fp8_tensor(K, None)
+    st = fwd(q=bad_data, k=good[1], v=good[2], dtype=DIT_DTYPE_FP8_E4M3)
+    assert st == DIT_ERR_NULL
+    st = fwd(q=good[0], k=bad_scale, v=good[2], dtype=DIT_DTYPE_FP8_E4M3)
+    assert st == DIT_ERR_NULL
+    mis = _lib.fp8_tensor(V, V + (1 << 30) + 2)
+    st = fwd(q=good[0], k=good[1], v=mis, dtype=DIT_DTYPE_FP8_E4M3)
+    assert st == DIT_ERR_ALIGN
+    mis = _lib.fp8_tensor(Q + 8, Q + (1 << 30))
+    st = fwd(q=mis, k=good[1], v=good[2], dtype=DIT_DTYPE_FP8_E4M3)
+    assert st == DIT_ERR_ALIGN
+    # output overlapping a scale array
+    st = fwd(q=good[0], k=good[1], v=good[2], o=K + (1 << 30), dtype=DIT_DTYPE_FP8_E4M3)
+    assert st == DIT_ERR_ALIAS
+
+
+def merge(o_parts=None, lse_parts=None, n=2, o=O, lse=L, B=1, H=2, Sq=100, d=64):
+    if o_parts is None:
+        o_parts = [Q, K]
+    if lse_parts is None:
+        lse_parts = [V, V + (1 << 20)]
+    return _lib.dit_attn_merge_status(o_parts, lse_parts, n, o, lse, B, H, Sq, d, stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), DIT_ERR_NULL), (dict(lse=None), DIT_ERR_NULL),
+    (dict(o_parts=[Q, None]), DIT_ERR_NULL), (dict(lse_parts=[None, V]), DIT_ERR_NULL),
+    (dict(n=0), DIT_ERR_UNSUPPORTED), (dict(n=17, o_parts=[Q] * 17, lse_parts=[V] * 17),
+                                       DIT_ERR_UNSUPPORTED),
+    (dict(d=32), DIT_ERR_UNSUPPORTED),
+    (dict(B=0), DIT_ERR_SHAPE), (dict(Sq=-1), DIT_ERR_SHAPE),
+    (dict(o=O + 4), DIT_ERR_ALIGN), (dict(lse=L + 1), DIT_ERR_ALIGN),
+    (dict(o_parts=[Q, K + 8]), DIT_ERR_ALIGN),
+    (dict(o=K + 256), DIT_ERR_ALIAS),           # partial overlap with part 1
+    (dict(lse=V + 64), DIT_ERR_ALIAS),          # partial overlap with lse part 0
+    (dict(o=V), DIT_ERR_ALIAS),                 # output O over an LSE input
+    (dict(lse=L, o=L - 512), DIT_ERR_ALIAS),    # O and LSE overlap each other
+])
+def test_merge_rejects(kw, status):
+    assert merge(**kw) == status
+
+
+def test_merge_null_arrays():
+    lib = _lib.load()
+    assert lib.dit_attn_merge(None, None, 2, O, L, 1, 2, 100, 64, None) == DIT_ERR_NULL
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, O, L, 1, 2, 256, 64), DIT_ERR_NULL), ((Q, None, L, 1, 2, 256, 64), DIT_ERR_NULL),
+    ((Q, O, None, 1, 2, 256, 64), DIT_ERR_NULL),
+    ((Q, O, L, 1, 2, 256, 80), DIT_ERR_UNSUPPORTED),
+    ((Q, O, L, 0, 2, 256, 64), DIT_ERR_SHAPE), ((Q, O, L, 1, 2, 0, 64), DIT_ERR_SHAPE),
+    ((Q + 2, O, L, 1, 2, 256, 64), DIT_ERR_ALIGN), ((Q, O + 8, L, 1, 2, 256, 64), DIT_ERR_ALIGN),
+    ((Q, O, L + 2, 1, 2, 256, 64), DIT_ERR_ALIGN),
+    ((Q, Q + 1024, L, 1, 2, 256, 64), DIT_ERR_ALIAS), ((Q, O, O + 16, 1, 2, 256, 64),
+                                                       DIT_ERR_ALIAS),
+])
+def test_quant_rejects(args, status):
+    assert _lib.dit_quant_fp8_status(*args, stream=0) == status
+
+
+def test_binding_raises_with_status():
+    with pytest.raises(_lib.DitError) as e:
+        _lib.dit_attn_fwd(None, K, V, O, L, 1, 2, 256, 256, 64, 0.125, DIT_DTYPE_BF16, stream=0)
+    assert e.value.status == DIT_ERR_NULL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(_lib.LibraryNotBuilt):
+        _lib.dit_version()
