@@ -88,10 +88,37 @@ __device__ __forceinline__ float log2_fast(float x)
     return __builtin_amdgcn_logf(x);
 }
 
-// Swap with the lane 32 positions away (lane l <-> l ^ 32).
-__device__ __forceinline__ float xor32(float x)
+// The value held by lane l ^ 32.  v_permlane32_swap(a, b) swaps the upper 32
+// lanes of a with the lower 32 lanes of b; with a = b = x the first result is
+// x[l % 32] and the second x[32 + l % 32] in every lane, so the partner's value
+// is the second result in the lower half and the first in the upper half.
+// (The selection by half is written out explicitly: combining the two results
+// directly, e.g. fmaxf(r0, r1), is mis-simplified to r0 by the compiler.)
+__device__ __forceinline__ float partner32(float x, bool upper_half)
 {
-    return __shfl_xor(x, 32, 64);
+    const int xi = __builtin_bit_cast(int, x);
+    const auto p = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return __builtin_bit_cast(float, upper_half ? p[0] : p[1]);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane s supplies the
+// address of 4 consecutive 16-bit elements; lane i of the group receives, in
+// slot j, element (i % 4) of the 4 read by lane 4j + i/4.  With lane s pointing
+// at row s/4, columns 4(s%4)..+3 of a row-major tile, lane i gets column i of
+// rows 0..3: a 4 x 16 block arrives transposed.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ld_lds_tr16(const void* p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Wait until every outstanding vector-memory operation of this wave (including
+// global -> LDS copies) has completed.
+__device__ __forceinline__ void wait_vmem_all()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)

@@ -67,10 +67,17 @@ def cpu_baseline(W, g, budget_s):
     keys) of the same workload; report its TFLOP/s."""
     import oracle
     from attention_non_causal_amd import workloads as wl
+    # two-point calibration: a call has a fixed cost (decoding the bf16
+    # tensors) plus a cost per query row
     t0 = time.perf_counter()
     oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=[0])
     t1 = time.perf_counter() - t0
-    n = int(max(1, min(W.Sq, budget_s / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=list(range(1, 17)))
+    t16 = time.perf_counter() - t0
+    per_row = max((t16 - t1) / 15, 1e-4)
+    fixed = max(t1 - per_row, 0.0)
+    n = int(max(1, min(W.Sq, (budget_s - fixed) / per_row)))
     rows = wl.sample_rows(W.Sq, n)
     t0 = time.perf_counter()
     oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
@@ -102,6 +109,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0: skip)")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain device-to-device copy of 1 GiB, whose HBM "
+                         "counters calibrate FETCH_SIZE / WRITE_SIZE in a --pmc profile")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
@@ -115,6 +125,15 @@ def main():
 
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: one 1 GiB device-to-device copy done")
+        del src, dst
     W = wl.WORKLOADS[args.workload]
     log(f"{props.name}: {props.multi_processor_count} CUs; workload {W.name}: generating inputs")
     g = wl.generate(W)
