@@ -6,6 +6,7 @@ into attention_non_causal_amd/libditattn.so.  Run as a module or call build().
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import os
 import shutil
 import subprocess
@@ -60,6 +61,9 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # resolve every symbol now: a kernel whose host stub was not emitted shows
+    # up here as an undefined symbol instead of at the first load on a GPU host
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

@@ -114,6 +114,23 @@ __device__ __forceinline__ u32x2 ld_lds_tr16(const void* p)
     return __builtin_bit_cast(u32x2, v);
 }
 
+// Buffer resource over [base, base + bytes) for raw (unstrided) buffer loads;
+// an access past `bytes` reads zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Copy 16 bytes per lane from buffer offset voff + soff (soff wave-uniform) into
+// LDS at lds + 16 * lane (lds wave-uniform): buffer_load_dwordx4 ... lds.
+// (Non-template wrappers keep the host compilation away from the builtins.)
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                              uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             voff, soff, 0, 0);
+}
+
 // Wait until every outstanding vector-memory operation of this wave (including
 // global -> LDS copies) has completed.
 __device__ __forceinline__ void wait_vmem_all()
