@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int64_t kMaxBytes = int64_t(1) << 62;
+constexpr int64_t kMaxKvBytesPerBatch = (int64_t(1) << 32) - 1;
 
 bool aligned(const void* p, uintptr_t a)
 {
@@ -102,6 +103,9 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     const int64_t o_bytes = checked_bytes({B, Sq, H, d, 2});
     const int64_t lse_bytes = checked_bytes({B, H, Sq, 4});
     if (q_bytes < 0 || kv_bytes < 0 || o_bytes < 0 || lse_bytes < 0)
+        return DIT_ERR_SHAPE;
+    // K and V of one batch are addressed with 32-bit buffer offsets
+    if (kv_bytes / B > kMaxKvBytesPerBatch)
         return DIT_ERR_SHAPE;
     if (!(isfinite(scale) && scale > 0.f))
         return DIT_ERR_VALUE;

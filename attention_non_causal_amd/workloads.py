@@ -65,6 +65,12 @@ class Workload:
         return 4.0 * self.B * self.H * self.Sq * self.Skv * self.d
 
     @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes the forward pass must move at least once: Q, K, V read, O and
+        LSE written (bf16 tensors, fp32 LSE)."""
+        return 2 * self.B * self.H * self.d * (2 * self.Sq + 2 * self.Skv) + 4 * self.B * self.H * self.Sq
+
+    @property
     def chunk(self) -> int:
         assert self.Skv % self.n_chunks == 0
         return self.Skv // self.n_chunks

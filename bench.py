@@ -27,6 +27,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+# rocprofv3 summary of the dominant kernel and the sources it was taken from;
+# its traffic figure is reported only while those sources are unchanged
+PROFILE = os.path.join(ROOT, "profiles", "fwd_bf16_d128_flux.md")
+PROFILE_SOURCES = ("attention_non_causal_amd/csrc/fwd_bf16.hip",
+                   "attention_non_causal_amd/csrc/common.hpp")
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
@@ -89,6 +94,26 @@ def cpu_baseline(W, g, budget_s):
                       f"(d{W.d}, fp64) in {dt:.1f} s"}
 
 
+def profiled_traffic():
+    """HBM bytes per launch from the committed rocprofv3 summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by a plain-copy calibration), or None when the
+    kernel sources have changed since it was taken."""
+    import hashlib
+    import re
+    try:
+        text = open(PROFILE).read()
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for src in PROFILE_SOURCES:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    m_sha = re.search(r"source_sha256: ([0-9a-f]+)", text)
+    m_tr = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not m_sha or not m_tr or not h.hexdigest().startswith(m_sha.group(1)):
+        return None
+    return int(m_tr.group(1))
+
+
 def bench_fwd(W, g, dev, steps, warmup):
     import torch
     from attention_non_causal_amd import functional as F
@@ -103,8 +128,8 @@ def bench_fwd(W, g, dev, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="flux")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0: skip)")
@@ -171,8 +196,9 @@ def main():
                    "d": W.d, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "fwd_bf16_kernel<128>",
-                     "kernel_ms": round(kern_ms, 4)},
+                     "traffic": profiled_traffic(), "traffic_unit": "bytes/launch",
+                     "algorithmic_bytes": W.algorithmic_bytes,
+                     "kernel": "fwd_bf16_kernel<128>", "kernel_ms": round(kern_ms, 4)},
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "extras": extras,

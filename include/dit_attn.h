@@ -54,7 +54,8 @@ extern "C" {
 enum dit_status {
     DIT_OK = 0,
     DIT_ERR_NULL = 1,        /* a required pointer is NULL                         */
-    DIT_ERR_SHAPE = 2,       /* B, H, Sq, Skv or S < 1, or a size overflows 2^62 B  */
+    DIT_ERR_SHAPE = 2,       /* B, H, Sq, Skv or S < 1, a size overflows 2^62 B, or
+                                one batch of K (or V) exceeds 2^32 - 1 bytes        */
     DIT_ERR_UNSUPPORTED = 3, /* d not 64/128, unknown dtype, n_parts not in 1..16   */
     DIT_ERR_ALIGN = 4,       /* tensor not 16-byte aligned (LSE/scales: 4-byte)    */
     DIT_ERR_VALUE = 5,       /* scale not finite or not > 0                        */
@@ -90,7 +91,8 @@ typedef struct dit_fp8_tensor {
  *       before P.V and the row sum uses the same rounded values.
  *   o:   device, bf16 [B][Sq][H][d] (fp32 result rounded to nearest even).
  *   lse: device, fp32 [B][H][Sq].
- *   d:   64 or 128.  Sq, Skv >= 1 (any value: tails are masked).
+ *   d:   64 or 128.  Sq, Skv >= 1 (any value: tails are masked).  One batch of K
+ *        (Skv * H * d elements) must fit in 2^32 - 1 bytes.
  *   scale: the softmax scale (e.g. 1/sqrt(d)), finite and > 0; used as given.
  *   o and lse must not overlap q, k, v or each other (DIT_ERR_ALIAS).
  */

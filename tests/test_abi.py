@@ -52,6 +52,8 @@ def test_version_and_status_strings():
     (dict(B=0), DIT_ERR_SHAPE), (dict(H=0), DIT_ERR_SHAPE), (dict(Sq=0), DIT_ERR_SHAPE),
     (dict(Skv=0), DIT_ERR_SHAPE), (dict(Skv=-5), DIT_ERR_SHAPE),
     (dict(B=1 << 30, H=1 << 30, Sq=1 << 30), DIT_ERR_SHAPE),
+    (dict(H=64, Skv=1 << 18, d=128), DIT_ERR_SHAPE),      # 4 GiB of K per batch
+    (dict(B=4, H=64, Skv=(1 << 18) - 1, d=128, scale=0.0), DIT_ERR_VALUE),  # just below
     (dict(scale=0.0), DIT_ERR_VALUE), (dict(scale=-0.125), DIT_ERR_VALUE),
     (dict(scale=math.inf), DIT_ERR_VALUE), (dict(scale=math.nan), DIT_ERR_VALUE),
     (dict(q=Q + 8), DIT_ERR_ALIGN), (dict(k=K + 2), DIT_ERR_ALIGN), (dict(v=V + 4), DIT_ERR_ALIGN),
