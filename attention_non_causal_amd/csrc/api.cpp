@@ -161,7 +161,7 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     a.scale = scale;
     if (dtype == DIT_DTYPE_BF16)
         return map_hip(dit::launch_fwd_bf16(a, stream));
-    return DIT_ERR_UNSUPPORTED;
+    return map_hip(dit::launch_fwd_fp8(a, stream));
 }
 
 int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, int n_parts,

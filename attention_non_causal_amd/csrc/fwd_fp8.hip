@@ -1,0 +1,431 @@
+// fwd_fp8.hip -- non-causal attention forward pass (O + LSE) on e4m3 inputs
+// with per-(b, h, 128-token block) fp32 scales, for gfx950 (CDNA4) fp8 MFMA.
+//
+// The FP8 attention backend of "AMD、Radeon AI PRO R9700S最大4台で..." (quick-start
+// flags and tuning section) runs attention on FP8 activations natively; the
+// block-scaled format follows "生成AI推論を速くするための設計ノート" sec. 3
+// (payload + block scales).  Inputs come from dit_quant_fp8:
+//     x[b,s,h,c] ~= e4m3(x8[b,s,h,c]) * scale[b,h,s/128].
+// What is computed is the same attention as the bf16 kernel (softmax(scale *
+// Q K^T) V and LSE), on the dequantised inputs, with P rounded to e4m3 for P.V.
+//
+// Work decomposition (mirrors the bf16 kernel): 4 waves x 32 query rows per
+// workgroup, 64-key tiles double-buffered in LDS through buffer_load ... lds.
+//   S^T = K8 Q8^T on v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0 scales); the
+//     fp32 block scales are uniform per (query tile, key tile) because both
+//     tiles sit inside one 128-token block, so q_scale * k_scale * scale *
+//     log2(e) becomes the coefficient of the softmax FMA.
+//   Softmax as in the bf16 kernel (log2 domain, lazy rescale with a 2^2
+//     threshold, so every weight is <= 4 and stays in e4m3's normal range).
+//   O^T += V8^T P^T on the same MFMA.  The V block scale v_s = 2^e * f
+//     (f in [1,2)) is split: f and the constant K = 448 / 2^3 go into the
+//     exponent (P'' = P * f * K = exp2(s*c - m + log2(f*K)) <= 448, rounded to
+//     e4m3), 2^e goes into the MFMA's E8M0 scale of P.  O_acc then collects
+//     K * sum_j P~_j v_j with P~ the rounded weights.  O is normalised by the
+//     sum of the same rounded weights (so O is a convex combination of the
+//     values and a single key returns its value), taken by one more MFMA per
+//     tile against an all-ones operand; LSE uses the sum of the unrounded
+//     weights, which keeps it exact up to fp32 rounding.
+//   P^T operand: the S^T accumulator gives lane (n, half) keys 8q + 4*half +
+//     0..3 in register group q; after packing to e4m3 (4 keys per dword), one
+//     v_permlane32_swap per pair of groups makes lane half g hold keys
+//     16t + 8g + 0..7, matching the V operand read with ds_read_b64_tr_b8 (a
+//     16-lane group reads 8 key rows x 16 channels and lane i receives channel
+//     i of the 8 rows).
+//   LDS rows hold d e4m3 bytes; chunk c of row r sits at slot c ^ h(r) (see
+//   fp8_slot) so the 16-row K reads and the 8-row transpose reads are free of
+//   bank conflicts.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dit {
+namespace {
+
+template <int D>
+struct FwdFp8Cfg {
+    static constexpr int kWaves = 4;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kBr = 32 * kWaves;               // query rows per workgroup
+    static constexpr int kBc = 64;                        // keys per tile
+    static constexpr int kRowBytes = D;                   // one e4m3 row
+    static constexpr int kChunks = D / 16;                // 16-byte chunks per row
+    static constexpr int kTileBytes = kBc * kRowBytes;
+    static constexpr int kBufBytes = 2 * kTileBytes;      // K tile then V tile
+    static constexpr int kLoads = kTileBytes / (16 * kThreads);
+    static constexpr int kMB = D / 32;                    // 32-channel output blocks
+    static constexpr int kKSteps = D / 64;                // MFMA k-steps of Q.K^T
+    static constexpr float kRescaleThreshold = 2.0f;      // log2 units: weights <= 4
+    static constexpr float kPScale = 56.0f;               // 448 / 2^(threshold + 1)
+    static constexpr int kScaleBlock = 128;               // tokens per block scale
+};
+
+// Chunk slot of chunk c in row r.
+template <int D>
+__device__ __forceinline__ int fp8_slot(int r, int c)
+{
+    if constexpr (D == 128) {
+        const int u = (r >> 1) & 7;
+        return c ^ (((u & 3) << 1) | (u >> 2));
+    } else {
+        const int u = (r >> 2) & 3;
+        return c ^ (((u & 1) << 1) | (u >> 1));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ int fp8_lds_byte(int r, int col)
+{
+    return r * D + fp8_slot<D>(r, col >> 4) * 16 + (col & 15);
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c, int scale_b)
+{
+    // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0 for A
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
+}
+
+// Four transpose reads (8 bytes each) at a + OFF + t * ROW16, t = 0..3,
+// completed before return.
+template <int OFF, int ROW16>
+__device__ __forceinline__ i32x8 tr8_read4(int a)
+{
+    u32x2 o0, o1, o2, o3;
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %4 offset:%5\n\t"
+        "ds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b8 %2, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b8 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3)
+        : "v"(a), "i"(OFF), "i"(OFF + ROW16), "i"(OFF + 2 * ROW16), "i"(OFF + 3 * ROW16)
+        : "memory");
+    i32x8 r;
+    r[0] = (int)o0[0]; r[1] = (int)o0[1]; r[2] = (int)o1[0]; r[3] = (int)o1[1];
+    r[4] = (int)o2[0]; r[5] = (int)o2[1]; r[6] = (int)o3[0]; r[7] = (int)o3[1];
+    return r;
+}
+
+// Pack 4 fp32 into 4 e4m3 bytes (round to nearest even; inputs <= 448).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+template <int D>
+struct FwdFp8Tile {
+    using Cfg = FwdFp8Cfg<D>;
+    static constexpr int kBc = Cfg::kBc;
+    static constexpr int kTile = Cfg::kTileBytes;
+    static constexpr int kMB = Cfg::kMB;
+
+    uint8_t* smem;
+    __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
+    uint32_t tok_bytes;
+    int Skv, n_kt, wave, hh;
+    float qc;                // q_scale * scale * log2(e) of this query tile
+    const float* ks;         // k scales of this (b, h)
+    const float* vs;         // v scales of this (b, h)
+    int ld_row[Cfg::kLoads];
+    uint32_t ld_voff[Cfg::kLoads];
+    i32x8 qf[Cfg::kKSteps];
+    int k_addr[Cfg::kKSteps][2];
+    int v_addr[kMB];
+    f32x16 oacc[kMB];
+    float m_used;  // log2-domain maximum the weights are taken against
+    float l_run;   // running sum of unrounded weights over this lane's keys
+    float lr_run;  // running sum of the e4m3-rounded weights over all keys
+
+    template <int BUF>
+    __device__ __forceinline__ void issue(int kt_next)
+    {
+        const int key0 = kt_next * kBc;
+        const uint32_t soff = (uint32_t)key0 * tok_bytes;
+        uint8_t* base = smem + BUF * Cfg::kBufBytes;
+        if (key0 + kBc <= Skv) {
+#pragma unroll
+            for (int i = 0; i < Cfg::kLoads; ++i) {
+                uint8_t* dst = base + (i * Cfg::kWaves + wave) * 1024;
+                copy16_to_lds(k_rsrc, dst, ld_voff[i], soff);
+                copy16_to_lds(v_rsrc, dst + kTile, ld_voff[i], soff);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < Cfg::kLoads; ++i) {
+                uint8_t* dst = base + (i * Cfg::kWaves + wave) * 1024;
+                const int over = max(key0 + ld_row[i] - (Skv - 1), 0);
+                const uint32_t vo = ld_voff[i] - (uint32_t)over * tok_bytes;
+                copy16_to_lds(k_rsrc, dst, vo, soff);
+                copy16_to_lds(v_rsrc, dst + kTile, vo, soff);
+            }
+        }
+    }
+
+    template <int BUF>
+    __device__ __forceinline__ void step(int kt)
+    {
+        constexpr int KOFF = BUF * Cfg::kBufBytes;
+        constexpr int VOFF = KOFF + kTile;
+        const int key0 = kt * kBc;
+        if (kt + 1 < n_kt)
+            issue<BUF ^ 1>(kt + 1);
+        const uint8_t* sm = smem;
+
+        // block scales of this key tile (uniform): both lie in block key0/128
+        const int kblk = key0 / Cfg::kScaleBlock;
+        const float c = qc * ks[kblk];
+        const uint32_t vbits = __builtin_bit_cast(uint32_t, vs[kblk]);
+        const int vexp = max((int)((vbits >> 23) & 0xff), 1);          // E8M0 exponent of v_s
+        const float vmant = vs[kblk] * __builtin_bit_cast(float, (uint32_t)(254 - vexp) << 23);
+        const float lift = log2_fast(vmant * Cfg::kPScale);            // log2(f * K)
+
+        // S^T = K8 Q8^T for two 32-key blocks
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int s = 0; s < Cfg::kKSteps; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 lo = ld_lds16(sm + k_addr[s][0] + KOFF + 32 * kb * D);
+                const u32x4 hi = ld_lds16(sm + k_addr[s][1] + KOFF + 32 * kb * D);
+                i32x8 a;
+                a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
+                a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
+                sacc[kb] = mfma_fp8_32x32x64(a, qf[s], sacc[kb], 127);
+            }
+        if (key0 + kBc > Skv) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+                    if (key >= Skv)
+                        sacc[kb][r] = -INFINITY;
+                }
+        }
+
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, partner32(mx, hh));
+        const float m_tile = mx * c;
+        const bool grow = m_tile > m_used + Cfg::kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_tile : m_used;
+            const float alpha = exp2_fast(m_used - m_new);
+            m_used = m_new;
+            l_run *= alpha;
+            lr_run *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb)
+                oacc[mb] *= alpha;
+        }
+
+        // P'' = P * f * K, rounded to e4m3; the LSE sum takes P itself.
+        const float m_eff = m_used - lift;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -m_eff));
+                sacc[kb][r] = p;
+                lsum += p;
+            }
+        const float inv_fk = __builtin_amdgcn_rcpf(vmant * Cfg::kPScale);
+        l_run += lsum * inv_fk;
+
+        // pack: dword q of block kb = keys 32kb + 8q + 4hh + 0..3
+        uint32_t pw[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pw[kb][q] = pack_e4m3x4(sacc[kb][4 * q], sacc[kb][4 * q + 1],
+                                        sacc[kb][4 * q + 2], sacc[kb][4 * q + 3]);
+        // regroup so lane half g holds keys 16t + 8g + 0..7 in dwords (2t, 2t+1)
+        i32x8 pf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(
+                    (int)pw[kb][2 * t2], (int)pw[kb][2 * t2 + 1], false, false);
+                pf[2 * (2 * kb + t2)] = sw[0];
+                pf[2 * (2 * kb + t2) + 1] = sw[1];
+            }
+
+        // O^T += V8^T P''^T, P'' carrying the 2^e part of the V block scale
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) {
+            const i32x8 va = tr8_read4<VOFF, 16 * D>(v_addr[mb]);
+            oacc[mb] = mfma_fp8_32x32x64(va, pf, oacc[mb], vexp);
+        }
+
+        // Sum of the rounded weights of this tile: every row of ones^T P''^T
+        // holds it (the same value in both lane halves).  It is taken after the
+        // transpose reads and consumed at once (all of its result registers are
+        // read, which waits for the whole MFMA): the transpose reads are written
+        // out in asm, and registers freed by a partly consumed MFMA result that
+        // is still in flight must never be handed to them.
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                                0x38383838, 0x38383838, 0x38383838, 0x38383838};
+            const f32x16 rs = mfma_fp8_32x32x64(ones, pf, f32x16{}, 127);
+            float all = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                all += rs[r];
+            lr_run += all * (1.0f / 16) * inv_fk;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        wait_vmem_all();
+        __syncthreads();
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int Sq, int Skv, float scale_log2,
+    int n_qtiles, int n_blocks)
+{
+    using Cfg = FwdFp8Cfg<D>;
+    constexpr int kMB = Cfg::kMB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::kBufBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int n = lane & 31;
+    const int hh = lane >> 5;
+
+    const int logical = xcd_remap(blockIdx.x, n_blocks);
+    const int qt = logical % n_qtiles;
+    const int bh = logical / n_qtiles;
+    const int h = bh % H;
+    const int b = bh / H;
+    const long tok = (long)H * D;  // bytes between consecutive tokens
+    const int nqb = (Sq + Cfg::kScaleBlock - 1) / Cfg::kScaleBlock;
+    const int nkb = (Skv + Cfg::kScaleBlock - 1) / Cfg::kScaleBlock;
+
+    FwdFp8Tile<D> st;
+    st.smem = smem;
+    st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    st.hh = hh;
+    st.Skv = Skv;
+    st.n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
+    st.tok_bytes = (uint32_t)tok;
+    // the query tile of 128 rows is exactly query block qt
+    st.qc = QS[(long)bh * nqb + qt] * scale_log2;
+    st.ks = KS + (long)bh * nkb;
+    st.vs = VS + (long)bh * nkb;
+    {
+        const uint8_t* Kbh = K + ((long)b * Skv * H + h) * D;
+        const uint8_t* Vbh = V + ((long)b * Skv * H + h) * D;
+        const int extent = (int)((uint32_t)(Skv - 1) * st.tok_bytes + D);
+        st.k_rsrc = make_rsrc(Kbh, extent);
+        st.v_rsrc = make_rsrc(Vbh, extent);
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::kLoads; ++i) {
+        const int p = (i * Cfg::kWaves + st.wave) * 64 + lane;
+        const int r = p / Cfg::kChunks;
+        st.ld_row[i] = r;
+        st.ld_voff[i] = (uint32_t)r * st.tok_bytes + fp8_slot<D>(r, p % Cfg::kChunks) * 16;
+    }
+    st.template issue<0>(0);
+
+    const int q_row = qt * Cfg::kBr + st.wave * 32 + n;
+    if (q_row < Sq) {
+        const uint8_t* src = Q + ((long)b * Sq * H + h) * D + (long)q_row * tok + 32 * hh;
+#pragma unroll
+        for (int s = 0; s < Cfg::kKSteps; ++s) {
+            const u32x4 lo = ld_global16(src + 64 * s);
+            const u32x4 hi = ld_global16(src + 64 * s + 16);
+            st.qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < Cfg::kKSteps; ++s)
+            st.qf[s] = i32x8{};
+    }
+
+    // K operand (A of S^T), step s: row n (+32 for the second block), bytes
+    // 64s + 32hh .. +31 (two chunks).  V transpose reads, block mb: lane group
+    // (hh, g2 = (lane/16)%2) reads rows 8hh + (lane%16)/2 (+16t) at channels
+    // 32mb + 16g2 + 8(lane%2) .. +7.
+#pragma unroll
+    for (int s = 0; s < Cfg::kKSteps; ++s)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            st.k_addr[s][e] = fp8_lds_byte<D>(n, 64 * s + 32 * hh + 16 * e);
+    {
+        const int vr = 8 * hh + ((lane & 15) >> 1);
+        const int vc = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+            st.v_addr[mb] = fp8_lds_byte<D>(vr, 32 * mb + vc);
+    }
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+        st.oacc[mb] = f32x16{};
+    st.m_used = -INFINITY;
+    st.l_run = 0.f;
+    st.lr_run = 0.f;
+
+    wait_vmem_all();
+    __syncthreads();
+
+    for (int kt = 0; kt < st.n_kt; kt += 2) {
+        st.template step<0>(kt);
+        if (kt + 1 < st.n_kt)
+            st.template step<1>(kt + 1);
+    }
+
+    const float l_tot = st.l_run + partner32(st.l_run, hh);
+    const float inv = 1.f / (st.lr_run * Cfg::kPScale);
+    if (q_row < Sq) {
+        uint16_t* dst = O + ((long)b * Sq * H + h) * D + (long)q_row * tok + 4 * hh;
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(st.oacc[mb][4 * g + 0] * inv, st.oacc[mb][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(st.oacc[mb][4 * g + 2] * inv, st.oacc[mb][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g) = w;
+            }
+        if (hh == 0)
+            LSE[((long)b * H + h) * Sq + q_row] = (st.m_used + log2_fast(l_tot)) * kLn2;
+    }
+}
+
+template <int D>
+hipError_t launch_fwd_fp8_d(const FwdArgs& a, hipStream_t stream)
+{
+    using Cfg = FwdFp8Cfg<D>;
+    const int n_qtiles = (a.Sq + Cfg::kBr - 1) / Cfg::kBr;
+    const long n_blocks = (long)n_qtiles * a.H * a.B;
+    if (n_blocks > 0x7fffffffL)
+        return hipErrorInvalidConfiguration;
+    const float scale_log2 = a.scale * kLog2e;
+    return launch_kernel(fwd_fp8_kernel<D>, dim3((unsigned)n_blocks), dim3(Cfg::kThreads),
+                         stream, a.q, a.k, a.v, a.q_scale, a.k_scale, a.v_scale, a.o, a.lse, a.H,
+                         a.Sq, a.Skv, scale_log2, n_qtiles, (int)n_blocks);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream)
+{
+    return a.d == 64 ? launch_fwd_fp8_d<64>(a, stream) : launch_fwd_fp8_d<128>(a, stream);
+}
+
+}  // namespace dit

@@ -244,17 +244,46 @@ def run_extras(dev, steps, warmup):
         f"{mms:.3f} ms = {res['wan_ring']['merge_GBs']} GB/s")
     del q, k, v, parts, o, lse
 
+    # fp8: the FLUX-like shape with 1% x8 outlier channels, quantised per
+    # (head, 128-token block); attention alone vs the fp8 peak, and the layer
+    # (three quantiser launches + attention)
     W = wl.WORKLOADS["flux_fp8"]
     g = wl.generate(W)
-    x = to_dev(g["k"], dev)
-    x8 = torch.empty(x.shape, dtype=torch.uint8, device=dev)
-    sc = torch.empty((W.B, W.H, (W.Skv + 127) // 128), dtype=torch.float32, device=dev)
-    _, qevs = time_launches(lambda: _lib.dit_quant_fp8(x, x8, sc, W.B, W.H, W.Skv, W.d), steps,
-                            warmup)
+    q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)
+    del g
+    nblk = (W.Skv + 127) // 128
+    bufs = {n: (torch.empty(t.shape, dtype=torch.uint8, device=dev),
+                torch.empty((W.B, W.H, nblk), dtype=torch.float32, device=dev))
+            for n, t in (("q", q), ("k", k), ("v", v))}
+    o = torch.empty_like(q)
+    lse = torch.empty((W.B, W.H, W.Sq), dtype=torch.float32, device=dev)
+
+    def quant_all():
+        for n, t in (("q", q), ("k", k), ("v", v)):
+            _lib.dit_quant_fp8(t, bufs[n][0], bufs[n][1], W.B, W.H, t.shape[1], W.d)
+
+    def attn_fp8():
+        F.attention_fp8(bufs["q"][0], bufs["q"][1], bufs["k"][0], bufs["k"][1], bufs["v"][0],
+                        bufs["v"][1], W.scale, out=o, lse=lse)
+
+    quant_all()
+    _, qevs = time_launches(lambda: _lib.dit_quant_fp8(k, bufs["k"][0], bufs["k"][1], W.B, W.H,
+                                                       W.Skv, W.d), steps, warmup)
     qms = float(np.mean(qevs))
-    qbytes = W.B * W.Skv * W.H * W.d * 3 + sc.numel() * 4
+    qbytes = W.B * W.Skv * W.H * W.d * 3 + nblk * W.B * W.H * 4
     res["quant_fp8"] = {"kernel_ms": round(qms, 4), "GBs": round(qbytes / qms / 1e6, 1)}
     log(f"extra quant_fp8 (one tensor): {qms:.4f} ms = {res['quant_fp8']['GBs']} GB/s")
+    _, aevs = time_launches(attn_fp8, steps, warmup)
+    ams = float(np.mean(aevs))
+    _, levs = time_launches(lambda: (quant_all(), attn_fp8()), steps, warmup)
+    lms = float(np.mean(levs))
+    res["flux_fp8"] = {"kernel_ms": round(ams, 4), "tflops": round(W.flops / ams / 1e9, 1),
+                       "pct_of_fp8_peak": round(100 * W.flops / ams / 1e9 / PEAK_FP8_TFLOPS, 2),
+                       "layer_ms_with_quant": round(lms, 4),
+                       "layer_tflops_with_quant": round(W.flops / lms / 1e9, 1)}
+    log(f"extra flux_fp8: attention {ams:.3f} ms = {res['flux_fp8']['tflops']} TFLOP/s "
+        f"({res['flux_fp8']['pct_of_fp8_peak']}% of fp8 peak); with 3 quantiser launches "
+        f"{lms:.3f} ms")
     return res
 
 
