@@ -11,32 +11,43 @@
 //
 // Work decomposition
 //   Workgroup = 4 wavefronts = 128 query rows of one (batch, head); each wave
-//   owns 32 rows.  Keys stream through LDS in tiles of 64, double-buffered:
-//   while a tile is consumed, the next is copied global -> LDS by
-//   buffer_load_dwordx4 ... lds (no VGPR staging).  Each lane's buffer offset
-//   within a tile is fixed for the whole kernel and the tile's start is a
-//   scalar offset, so a full tile costs no vector address arithmetic; the
-//   last, partial tile clamps its rows to the last key instead (every LDS value
-//   stays finite).  One barrier per tile separates producer and consumer.
-//   Per tile and wave:
+//   owns 32 rows.  Keys stream through LDS in tiles of 64.  Copies go global ->
+//   LDS by buffer_load_dwordx4 ... lds (no VGPR staging); each lane's buffer
+//   offset within a tile is fixed for the whole kernel and the tile's start is
+//   a scalar offset.  A tile past the last key clamps its rows to the last key,
+//   so every LDS value stays finite.
+//   Per tile and wave the matrix work is
 //     S^T (keys x queries) = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from
 //       LDS, B = Q^T held in registers for the whole kernel.  The transpose
 //       puts one query per lane column, so a row maximum or sum is a per-lane
 //       reduction plus one exchange with lane l^32 (v_permlane32_swap).
-//     Online softmax in the log2 domain: scale*log2(e) is folded into one FMA
-//       before v_exp_f32.  The output is rescaled only when a row maximum grows
-//       by more than 2^8 over the one in use; until then the stale maximum
-//       keeps every weight below 2^8, and the final O / sum and LSE are exact
-//       for any maximum, so this skips almost all rescale multiplies.
 //     O^T (channels x queries) += V^T P^T: A = V^T read from the row-major V
 //       tile with ds_read_b64_tr_b16 (LDS transpose read), B = P^T straight from
 //       the S^T accumulator registers.  A and B use the same assignment of keys
 //       to k slots, so no register shuffle is needed.
-//   LDS layout: rows of D bf16; the 16-byte chunk c of row r sits at chunk
-//   slot c ^ f(r), where f permutes bits of r so that both read patterns are
-//   free of bank conflicts -- 16 rows x one chunk (the K operand) and 4 rows
-//   x 4 chunks (the transpose read of V) each cover all 64 banks.  Every LDS
-//   address is a per-lane base (computed once) plus a compile-time offset.
+//   Software pipeline: iteration j runs the P V product of tile j-1, the K Q^T
+//   product of tile j+1 and the softmax of tile j.  The three are independent,
+//   so the 32 (d = 128) matrix instructions of an iteration alternate between
+//   the two products, and the softmax's vector instructions are spread over
+//   the same slots: the vector ALU works in the shadow of the matrix core
+//   instead of after it.  The slots are fenced (sched_barrier) so the compiler
+//   keeps that order.  LDS operands are read several slots ahead.
+//   Online softmax in the log2 domain: scale*log2(e) is folded into one FMA
+//   before v_exp_f32.  The output is rescaled only when a row maximum grows by
+//   more than 2^8 over the one in use; until then the stale maximum keeps every
+//   weight below 2^8, and the final O / sum and LSE are exact for any maximum,
+//   so this skips almost all rescale multiplies.  The rescale of O is applied
+//   at the end of the iteration, after the P V product of the previous tile
+//   (taken against the old maximum) has been accumulated.
+//   LDS: two K and two V tile buffers, each its own LDS object.  Iteration j
+//   reads K(j+1), V(j-1) from one pair while K(j+2), V(j) are copied into the
+//   other; one barrier per iteration.  (Separate objects also let the compiler
+//   see that the transpose reads never alias an outstanding copy.)
+//   Layout of a tile: rows of D bf16; the 16-byte chunk c of row r sits at
+//   chunk slot c ^ f(r), where f permutes bits of r so that both read patterns
+//   are free of bank conflicts -- 16 rows x one chunk (the K operand) and 4
+//   rows x 4 chunks (the transpose read of V) each cover all 64 banks.  Every
+//   LDS address is a per-lane base (computed once) plus a compile-time offset.
 //   Tails: query rows >= Sq are computed on zero queries and never stored;
 //   keys >= Skv get score -inf.
 #include "common.hpp"
@@ -56,6 +67,7 @@ struct FwdBf16Cfg {
     static constexpr int kTileBytes = kBc * kRowBytes;     // one K or V tile
     static constexpr int kBufBytes = 2 * kTileBytes;       // K tile then V tile
     static constexpr int kLoads = kTileBytes / (16 * kThreads);  // 16-B loads per thread
+    static constexpr int kLoadRows = 16 * kThreads / kRowBytes;   // rows one copy covers
     static constexpr int kMB = D / 32;                     // 32-channel output blocks
     static constexpr float kRescaleThreshold = 8.0f;       // log2 units
 };
@@ -78,50 +90,20 @@ __device__ __forceinline__ int lds_byte(int r, int col)
     return r * (D * 2) + swz_slot<D>(r, col >> 3) * 16 + (col & 7) * 2;
 }
 
-// N transpose reads at per-lane addresses a[i] + OFF, completed before return.
-// (Written out so the reads carry no implied dependence on the outstanding
-// global -> LDS copies into the other buffer.)
-template <int OFF>
-__device__ __forceinline__ void tr_read4(u32x2 (&o)[4], const int (&a)[4])
+// Keep a vector-ALU result where it is computed: an empty asm that reads and
+// rewrites it.  Without this the compiler sinks softmax work that feeds only
+// the next iteration into that iteration, past the branches at its start, and
+// the vector work ends up in one block instead of between the matrix
+// instructions.  (Only vector-ALU results are pinned: an asm reading an MFMA
+// result would make the compiler wait for the MFMA to finish.)
+__device__ __forceinline__ void pin(float& x)
 {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
-        : "memory");
+    asm volatile("" : "+v"(x));
 }
 
-template <int OFF>
-__device__ __forceinline__ void tr_read8(u32x2 (&o)[8], const int (&a)[8])
+__device__ __forceinline__ void pin(u32x4& x)
 {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
-          "=&v"(o[6]), "=&v"(o[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
-          "v"(a[7]), "i"(OFF)
-        : "memory");
-}
-
-template <int D, int OFF>
-__device__ __forceinline__ void tr_read(u32x2 (&o)[2 * D / 32], const int (&a)[2 * D / 32])
-{
-    if constexpr (D == 128)
-        tr_read8<OFF>(o, a);
-    else
-        tr_read4<OFF>(o, a);
+    asm volatile("" : "+v"(x));
 }
 
 // Per-thread state of one workgroup's pass over the keys.
@@ -129,82 +111,225 @@ template <int D>
 struct FwdBf16Tile {
     using Cfg = FwdBf16Cfg<D>;
     static constexpr int kBc = Cfg::kBc;
-    static constexpr int kTile = Cfg::kTileBytes;
     static constexpr int kRow = Cfg::kRowBytes;
     static constexpr int kMB = Cfg::kMB;
+    static constexpr int kSteps = D / 16;          // k steps of K Q^T
+    static constexpr int kSlots = D / 4;           // matrix instructions per iteration
+    static constexpr int kVReads = 2 * kMB;        // V^T transpose reads per 16-key step
 
-    uint8_t* smem;
+    uint8_t* kbuf[2];
+    uint8_t* vbuf[2];
     __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
     uint32_t tok_bytes;
     int Skv, n_kt, wave, hh;
     float scale_log2;
-    int ld_row[Cfg::kLoads];
-    uint32_t ld_voff[Cfg::kLoads];
-    bf16x8 qf[D / 16];
-    int k_addr[D / 16];
-    int v_addr[2 * kMB];
+    uint32_t ld_voff;        // this lane's offset in copy 0 (copy i: + i * kLoadRows rows)
+    bf16x8 qf[kSteps];
+    int k_addr[kSteps / 2];  // steps s and s + kSteps/2 differ in one address bit
+    int v_addr[kVReads];
     f32x16 oacc[kMB];
+    f32x16 sacc[2][2];       // [parity][32-key block]: S^T of a tile
+    bf16x8 pf[2][4];         // [parity][16-key step]: P^T of a tile
+    u32x2 vf[kVReads];       // V^T fragments of one 16-key step
+    bf16x8 kf[3];            // K fragments, three in flight
+    float mxc[4];            // partial row maxima
+    float lsum[2];           // partial row sums of the current tile
+    float alpha;             // rescale factor of this iteration
+    bool grow;
     float m_used;  // maximum (scale*log2(e) units) the weights are taken against
     float l_run;   // running sum over this lane's half of the keys
 
-    // Copy key tile kt_next into LDS buffer BUF (K tile, then V tile).
-    template <int BUF>
-    __device__ __forceinline__ void issue(int kt_next)
+    // Copy tile kt of K (to K buffer KB) and of V (to V buffer VB) into LDS;
+    // KB or VB < 0 skips that tensor.
+    template <int KB, int VB>
+    __device__ __forceinline__ void copy_tile(int kt)
     {
-        const int key0 = kt_next * kBc;
+        const int key0 = kt * kBc;
         const uint32_t soff = (uint32_t)key0 * tok_bytes;
-        uint8_t* base = smem + BUF * Cfg::kBufBytes;
         if (key0 + kBc <= Skv) {
 #pragma unroll
             for (int i = 0; i < Cfg::kLoads; ++i) {
-                uint8_t* dst = base + (i * Cfg::kWaves + wave) * 1024;
-                copy16_to_lds(k_rsrc, dst, ld_voff[i], soff);
-                copy16_to_lds(v_rsrc, dst + kTile, ld_voff[i], soff);
+                const int off = (i * Cfg::kWaves + wave) * 1024;
+                const uint32_t so = soff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes;
+                if constexpr (KB >= 0)
+                    copy16_to_lds(k_rsrc, kbuf[KB] + off, ld_voff, so);
+                if constexpr (VB >= 0)
+                    copy16_to_lds(v_rsrc, vbuf[VB] + off, ld_voff, so);
             }
         } else {
-            // partial tile: rows past the last key re-read the last key
+            // partial or past-the-end tile: rows past the last key re-read the last key
 #pragma unroll
             for (int i = 0; i < Cfg::kLoads; ++i) {
-                uint8_t* dst = base + (i * Cfg::kWaves + wave) * 1024;
-                const int over = max(key0 + ld_row[i] - (Skv - 1), 0);
-                const uint32_t vo = ld_voff[i] - (uint32_t)over * tok_bytes;
-                copy16_to_lds(k_rsrc, dst, vo, soff);
-                copy16_to_lds(v_rsrc, dst + kTile, vo, soff);
+                const int off = (i * Cfg::kWaves + wave) * 1024;
+                const int row = (wave * 64 + (int)(threadIdx.x & 63)) / Cfg::kChunks +
+                                i * Cfg::kLoadRows;
+                const int over = max(key0 + row - (Skv - 1), 0);
+                const uint32_t vo = ld_voff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes -
+                                    (uint32_t)over * tok_bytes;
+                if constexpr (KB >= 0)
+                    copy16_to_lds(k_rsrc, kbuf[KB] + off, vo, soff);
+                if constexpr (VB >= 0)
+                    copy16_to_lds(v_rsrc, vbuf[VB] + off, vo, soff);
             }
         }
     }
 
-    // O^T += V^T P^T for 16-key step T; the reads for half hi give slots 4hi..4hi+3.
-    template <int VOFF, int T>
-    __device__ __forceinline__ void pv_step(const bf16x8& p)
+    // LDS byte offset of the K operand of k step s (see k_addr).
+    __device__ __forceinline__ int k_off(int s) const
     {
-        u32x2 vf[2 * kMB];
-        tr_read<D, VOFF + 16 * T * kRow>(vf, v_addr);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-            oacc[mb] = mfma32x32x16(cat_bf16x8(vf[2 * mb], vf[2 * mb + 1]), p, oacc[mb]);
+        return s < kSteps / 2 ? k_addr[s] : (k_addr[s - kSteps / 2] ^ (16 * kSteps));
     }
 
-    // Consume key tile kt from LDS buffer BUF while tile kt+1 is copied into
-    // the other buffer.
-    template <int BUF>
-    __device__ __forceinline__ void step(int kt)
+    // K operand of K Q^T step q (k step q/2, 32-key block q%2) from K buffer KB.
+    template <int KB, int Q>
+    __device__ __forceinline__ void read_k()
     {
-        constexpr int KOFF = BUF * Cfg::kBufBytes;
-        constexpr int VOFF = KOFF + kTile;
-        const int key0 = kt * kBc;
-        if (kt + 1 < n_kt)
-            issue<BUF ^ 1>(kt + 1);
-        const uint8_t* sm = smem;
+        kf[Q % 3] = as_bf16x8(ld_lds16(kbuf[KB] + k_off(Q / 2) + 32 * (Q % 2) * kRow));
+    }
 
-        // S^T = K Q^T for two 32-key blocks.
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // Transpose read E (block E/2, half E%2) of 16-key step T from V buffer VB.
+    template <int VB, int T, int E>
+    __device__ __forceinline__ void read_v()
+    {
+        vf[E] = ld_lds_tr16(vbuf[VB] + v_addr[E] + 16 * T * kRow);
+    }
+
+    // The full S^T of one tile from K buffer KB into sacc[SP] (prologue only).
+    template <int KB, int SP>
+    __device__ __forceinline__ void qk_tile()
+    {
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
+        for (int s = 0; s < kSteps; ++s)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-                sacc[kb] = mfma32x32x16(
-                    as_bf16x8(ld_lds16(sm + k_addr[s] + KOFF + 32 * kb * kRow)), qf[s], sacc[kb]);
+                sacc[SP][kb] = mfma32x32x16(
+                    as_bf16x8(ld_lds16(kbuf[KB] + k_off(s) + 32 * kb * kRow)), qf[s],
+                    s == 0 ? f32x16{} : sacc[SP][kb]);
+    }
+
+    // Softmax of the tile in sacc[P], vector work of slot I.
+    //   slots 0-3: four chains of partial maxima over 8 scores each;
+    //   slot 4:    the row maximum (both lane halves);
+    //   slot 5:    the maximum in use and this iteration's rescale factor;
+    //   slots 6..: 8 groups of 4 scores -> weights, sums, bf16 pairs;
+    //   last slot: the tile's row sum.
+    template <int P, int I>
+    __device__ __forceinline__ void softmax_part()
+    {
+        constexpr int kPer = (kSlots - 8) / 8;  // slots per group of 4 scores
+        if constexpr (I < 4) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f32x16& s = sacc[P][c / 2];
+                const int o = 8 * (c % 2);
+                if constexpr (I == 0)
+                    mxc[c] = fmaxf(fmaxf(s[o + 0], s[o + 1]), s[o + 2]);
+                else if constexpr (I == 1)
+                    mxc[c] = fmaxf(fmaxf(mxc[c], s[o + 3]), s[o + 4]);
+                else if constexpr (I == 2)
+                    mxc[c] = fmaxf(fmaxf(mxc[c], s[o + 5]), s[o + 6]);
+                else
+                    mxc[c] = fmaxf(mxc[c], s[o + 7]);
+                pin(mxc[c]);
+            }
+        } else if constexpr (I == 4) {
+            float mx = fmaxf(fmaxf(mxc[0], mxc[1]), fmaxf(mxc[2], mxc[3]));
+            mxc[0] = fmaxf(mx, partner32(mx, hh));
+            pin(mxc[0]);
+        } else if constexpr (I == 5) {
+            const float m_tile = mxc[0] * scale_log2;
+            grow = m_tile > m_used + Cfg::kRescaleThreshold;
+            const float m_new = grow ? m_tile : m_used;
+            alpha = exp2_fast(m_used - m_new);
+            m_used = m_new;
+            pin(alpha);
+            pin(m_used);
+            lsum[0] = 0.f;
+            lsum[1] = 0.f;
+        } else if constexpr (I >= 6 && I < 6 + 8 * kPer) {
+            constexpr int G = (I - 6) / kPer;     // group of 4 scores
+            constexpr int sub = (I - 6) % kPer;
+            constexpr int kb = G / 4;
+            constexpr int r0 = 4 * (G % 4);
+            f32x16& s = sacc[P][kb];
+            if constexpr (kPer == 1) {
+#pragma unroll
+                for (int r = r0; r < r0 + 4; ++r) {
+                    float e = exp2_fast(__builtin_fmaf(s[r], scale_log2, -m_used));
+                    pin(e);
+                    s[r] = e;
+                }
+            } else if constexpr (sub < 2) {
+#pragma unroll
+                for (int r = r0 + 2 * sub; r < r0 + 2 * sub + 2; ++r) {
+                    float e = exp2_fast(__builtin_fmaf(s[r], scale_log2, -m_used));
+                    pin(e);
+                    s[r] = e;
+                }
+            }
+            if constexpr (sub == kPer - 1) {
+                lsum[G % 2] += (s[r0] + s[r0 + 1]) + (s[r0 + 2] + s[r0 + 3]);
+                pin(lsum[G % 2]);
+                // P^T fragment t = 16-key step: registers 8(t%2)..+7 of block t/2
+                constexpr int t = 2 * kb + (G % 4) / 2;
+                constexpr int w = 2 * (G % 2);
+                u32x4 v = __builtin_bit_cast(u32x4, pf[P][t]);
+                v[w] = pack_bf16x2(s[r0], s[r0 + 1]);
+                v[w + 1] = pack_bf16x2(s[r0 + 2], s[r0 + 3]);
+                pin(v);
+                pf[P][t] = as_bf16x8(v);
+            }
+        }
+    }
+
+    // Slot I of iteration parity P: one matrix instruction, the LDS reads
+    // for later slots, and a share of the softmax.
+    //   even I: O^T += V^T P^T, 16-key step t = I/(2 kMB), block mb
+    //           (P^T of the previous tile, V from buffer P^1);
+    //   odd I:  S^T += K Q^T for the next tile, k step q/2, 32-key block q%2
+    //           (K from buffer P^1).
+    template <int P, int I>
+    __device__ __forceinline__ void slot()
+    {
+        constexpr int v = I / 2;
+        if constexpr (I % 2 == 0) {
+            constexpr int t = v / kMB, mb = v % kMB;
+            oacc[mb] = mfma32x32x16(cat_bf16x8(vf[2 * mb], vf[2 * mb + 1]), pf[P ^ 1][t],
+                                    oacc[mb]);
+        } else {
+            constexpr int s = v / 2, kb = v % 2;
+            sacc[P ^ 1][kb] = mfma32x32x16(kf[v % 3], qf[s], s == 0 ? f32x16{} : sacc[P ^ 1][kb]);
+            if constexpr (v + 2 < 2 * kSteps)
+                read_k<P ^ 1, v + 2>();
+        }
+        // transpose read E of 16-key step t >= 1 in slot 2kMB(t-1) + E + 1, one
+        // slot after the step before has consumed fragment E
+        if constexpr (I >= 1) {
+            constexpr int t = (I - 1) / kVReads + 1, E = (I - 1) % kVReads;
+            if constexpr (t < 4)
+                read_v<P ^ 1, t, E>();
+        }
+        softmax_part<P, I>();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    template <int P, int I>
+    __device__ __forceinline__ void slots()
+    {
+        if constexpr (I < kSlots) {
+            slot<P, I>();
+            slots<P, I + 1>();
+        }
+    }
+
+    // Iteration kt (parity P = kt % 2): P V of tile kt-1, K Q^T of tile kt+1,
+    // softmax of tile kt; copies K(kt+2) and V(kt) into buffers P.
+    template <int P>
+    __device__ __forceinline__ void iteration(int kt)
+    {
+        copy_tile<-1, P>(kt);
+        copy_tile<P, -1>(kt + 2);
+        const int key0 = kt * kBc;
         if (key0 + kBc > Skv) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -212,59 +337,41 @@ struct FwdBf16Tile {
                 for (int r = 0; r < 16; ++r) {
                     const int key = key0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
                     if (key >= Skv)
-                        sacc[kb][r] = -INFINITY;
+                        sacc[P][kb][r] = -INFINITY;
                 }
         }
-
-        float mx = sacc[0][0];
+        // operands of the first slots
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                mx = fmaxf(mx, sacc[kb][r]);
-        mx = fmaxf(mx, partner32(mx, hh));
-        const float m_tile = mx * scale_log2;
-        const bool grow = m_tile > m_used + Cfg::kRescaleThreshold;
+        for (int e = 0; e < kVReads; ++e)
+            vf[e] = ld_lds_tr16(vbuf[P ^ 1] + v_addr[e]);
+        read_k<P ^ 1, 0>();
+        read_k<P ^ 1, 1>();
+        __builtin_amdgcn_sched_barrier(0);
+        slots<P, 0>();
+        l_run = __builtin_fmaf(l_run, alpha, lsum[0] + lsum[1]);
         if (__builtin_amdgcn_ballot_w64(grow)) {
-            const float m_new = grow ? m_tile : m_used;
-            const float alpha = exp2_fast(m_used - m_new);
-            m_used = m_new;
-            l_run *= alpha;
 #pragma unroll
             for (int mb = 0; mb < kMB; ++mb)
                 oacc[mb] *= alpha;
         }
-
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2_fast(__builtin_fmaf(sacc[kb][r], scale_log2, -m_used));
-                sacc[kb][r] = p;
-                lsum += p;
-            }
-        l_run += lsum;
-
-        // P^T fragments: 16-key step t takes registers 8*(t%2) .. +7 of block t/2;
-        // slot j is key 16t + 8(j/4) + 4*hh + (j%4).
-        bf16x8 pf[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            u32x4 w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                w[j] = pack_bf16x2(sacc[t / 2][8 * (t % 2) + 2 * j],
-                                   sacc[t / 2][8 * (t % 2) + 2 * j + 1]);
-            pf[t] = as_bf16x8(w);
-        }
-        pv_step<VOFF, 0>(pf[0]);
-        pv_step<VOFF, 1>(pf[1]);
-        pv_step<VOFF, 2>(pf[2]);
-        pv_step<VOFF, 3>(pf[3]);
-
         wait_vmem_all();
         __syncthreads();
+    }
+
+    // P V of the last tile (parity P), after the loop.
+    template <int P>
+    __device__ __forceinline__ void last_pv()
+    {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            u32x2 f[kVReads];
+#pragma unroll
+            for (int e = 0; e < kVReads; ++e)
+                f[e] = ld_lds_tr16(vbuf[P] + v_addr[e] + 16 * t * kRow);
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb)
+                oacc[mb] = mfma32x32x16(cat_bf16x8(f[2 * mb], f[2 * mb + 1]), pf[P][t], oacc[mb]);
+        }
     }
 };
 
@@ -277,8 +384,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     using Cfg = FwdBf16Cfg<D>;
     constexpr int kMB = Cfg::kMB;
     constexpr int kRow = Cfg::kRowBytes;
-    // [buffer][K tile, V tile]
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::kBufBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[Cfg::kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -293,7 +402,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const long tok = (long)H * D;  // elements between consecutive tokens
 
     FwdBf16Tile<D> st;
-    st.smem = smem;
+    st.kbuf[0] = k_lds0;
+    st.kbuf[1] = k_lds1;
+    st.vbuf[0] = v_lds0;
+    st.vbuf[1] = v_lds1;
     st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     st.hh = hh;
     st.Skv = Skv;
@@ -311,14 +423,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     // Copy i of wave w fills LDS chunks [(i*kWaves + w)*64, +64) of a tile; lane
     // l takes chunk p = that base + l, i.e. row p / kChunks at slot p % kChunks,
     // which holds column chunk (p % kChunks) ^ f(row).
-#pragma unroll
-    for (int i = 0; i < Cfg::kLoads; ++i) {
-        const int p = (i * Cfg::kWaves + st.wave) * 64 + lane;
+    // Copy i covers rows i * kLoadRows more than copy 0 and, as f() depends only on
+    // row bits that copy index does not change, the same chunk slots.
+    {
+        const int p = st.wave * 64 + lane;
         const int r = p / Cfg::kChunks;
-        st.ld_row[i] = r;
-        st.ld_voff[i] = (uint32_t)r * st.tok_bytes + swz_slot<D>(r, p % Cfg::kChunks) * 16;
+        st.ld_voff = (uint32_t)r * st.tok_bytes + swz_slot<D>(r, p % Cfg::kChunks) * 16;
     }
-    st.template issue<0>(0);
+    // K(0), K(1) for the first two K Q^T products; V(1) into V buffer 1, where
+    // the first iteration's P V (with P = 0) reads finite values.
+    st.template copy_tile<0, -1>(0);
+    st.template copy_tile<1, 1>(1);
 
     const int q_row = qt * Cfg::kBr + st.wave * 32 + n;
     if (q_row < Sq) {
@@ -338,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     // 32mb + 16(g%2) + 4(lane%4) .. +3, so lane l receives channel 32mb + l%32
     // of keys 16t + 8hi + 4hh + 0..3.
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
+    for (int s = 0; s < D / 32; ++s)
         st.k_addr[s] = lds_byte<D>(n, 16 * s + 8 * hh);
     {
         const int vr = 4 * hh + ((lane & 15) >> 2);
@@ -352,16 +467,27 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
         st.oacc[mb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        st.pf[1][t] = as_bf16x8(u32x4{0, 0, 0, 0});
     st.m_used = -INFINITY;
     st.l_run = 0.f;
 
     wait_vmem_all();
     __syncthreads();
+    st.template qk_tile<0, 0>();
+    __syncthreads();  // K buffer 0 is refilled by the first iteration
 
-    for (int kt = 0; kt < st.n_kt; kt += 2) {
-        st.template step<0>(kt);
-        if (kt + 1 < st.n_kt)
-            st.template step<1>(kt + 1);
+    int kt = 0;
+    for (; kt + 1 < st.n_kt; kt += 2) {
+        st.template iteration<0>(kt);
+        st.template iteration<1>(kt + 1);
+    }
+    if (kt < st.n_kt) {
+        st.template iteration<0>(kt);
+        st.template last_pv<0>();
+    } else {
+        st.template last_pv<1>();
     }
 
     const float l_tot = st.l_run + partner32(st.l_run, hh);
