@@ -42,9 +42,19 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags.  fwd_bf16.hip keeps O in accumulation registers through
+# asm MFMAs and wants every compiler-generated MFMA (the S^T products, read by
+# vector instructions) in the VGPR form; without NaN semantics its running
+# maxima compile to v_max3_f32 with no canonicalising instructions (a NaN
+# input gives a NaN result either way).
+FILE_FLAGS = {
+    "fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

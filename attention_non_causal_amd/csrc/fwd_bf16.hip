@@ -92,11 +92,14 @@ __device__ __forceinline__ int lds_byte(int r, int col)
 
 // Keep a vector-ALU result where it is computed: an empty asm that reads and
 // rewrites it.  Without this the compiler sinks softmax work that feeds only
-// the next iteration into that iteration, past the branches at its start, and
-// the vector work ends up in one block instead of between the matrix
-// instructions.  (Only vector-ALU results are pinned: an asm reading an MFMA
-// result would make the compiler wait for the MFMA to finish.)
+// the next iteration into that iteration, past the branches at its start, or
+// hoists it into an earlier slot.  (Only vector-ALU results are pinned.)
 __device__ __forceinline__ void pin(float& x)
+{
+    asm volatile("" : "+v"(x));
+}
+
+__device__ __forceinline__ void pin(uint32_t& x)
 {
     asm volatile("" : "+v"(x));
 }
@@ -104,6 +107,47 @@ __device__ __forceinline__ void pin(float& x)
 __device__ __forceinline__ void pin(u32x4& x)
 {
     asm volatile("" : "+v"(x));
+}
+
+// The matrix instructions of the tile loop are asm statements: then their
+// order against the slot fences is fixed (compiler-generated MFMAs have no such
+// ordering and get moved), O stays in accumulation registers (AGPRs) and the
+// S^T accumulators, which the softmax reads, in VGPRs.  The compiler does not
+// see these as MFMAs, so the kernel keeps the wait states itself: vector code
+// reads an S^T block at least two matrix instructions after its last step,
+// and touches O only after acc_wait (tests/test_asm_hazards.py checks the
+// generated code).
+//   O^T block += A B, accumulator in AGPRs.
+__device__ __forceinline__ void mfma_o(f32x16& acc, u32x4 a, u32x4 b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+//   S^T block = A B (first k step) or += A B, accumulator in VGPRs, B (Q^T,
+//   loop-invariant) in AGPRs.
+__device__ __forceinline__ void mfma_s0(f32x16& acc, u32x4 a, const u32x4& b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "a"(b));
+}
+
+__device__ __forceinline__ void mfma_s(f32x16& acc, u32x4 a, const u32x4& b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+
+// Wait states before vector code touches an O block after the asm MFMAs on it
+// (and before the next MFMA after vector code wrote it): 8 per block, the
+// blocks waited for one after another (an 8-pass MFMA needs at most 18).
+__device__ __forceinline__ void acc_wait(f32x16& acc)
+{
+    asm volatile("s_nop 7" : "+a"(acc));
+}
+
+// 24 wait states before vector code writes an S^T block an MFMA may still be
+// producing.
+__device__ __forceinline__ void vgpr_wait(f32x16& acc)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }
 
 // Per-thread state of one workgroup's pass over the keys.
@@ -116,6 +160,7 @@ struct FwdBf16Tile {
     static constexpr int kSteps = D / 16;          // k steps of K Q^T
     static constexpr int kSlots = D / 4;           // matrix instructions per iteration
     static constexpr int kVReads = 2 * kMB;        // V^T transpose reads per 16-key step
+    static constexpr int kPer = D == 128 ? 3 : 1;  // slots per group of 4 scores
 
     uint8_t* kbuf[2];
     uint8_t* vbuf[2];
@@ -124,53 +169,39 @@ struct FwdBf16Tile {
     int Skv, n_kt, wave, hh;
     float scale_log2;
     uint32_t ld_voff;        // this lane's offset in copy 0 (copy i: + i * kLoadRows rows)
-    bf16x8 qf[kSteps];
+    u32x4 qf[kSteps];        // bf16 operands are carried as raw 32-bit words
     int k_addr[kSteps / 2];  // steps s and s + kSteps/2 differ in one address bit
     int v_addr[kVReads];
     f32x16 oacc[kMB];
     f32x16 sacc[2][2];       // [parity][32-key block]: S^T of a tile
-    bf16x8 pf[2][4];         // [parity][16-key step]: P^T of a tile
+    u32x4 pf[2][4];          // [parity][16-key step]: P^T of a tile
     u32x2 vf[kVReads];       // V^T fragments of one 16-key step
-    bf16x8 kf[3];            // K fragments, three in flight
+    u32x4 kf[3];             // K fragments, three in flight
     float mxc[4];            // partial row maxima
-    float lsum[2];           // partial row sums of the current tile
+    uint32_t pw[2];          // bf16 pairs of the even group of a 16-key step
+    float lsum;              // sum of this lane's weights of the current tile
+    float m_tile;            // row maximum of the current tile (scale*log2(e) units)
     float alpha;             // rescale factor of this iteration
-    bool grow;
+    int grow;                // (an int: a bool member makes the optimizer carry its
+                             // neighbours as bytes)
     float m_used;  // maximum (scale*log2(e) units) the weights are taken against
     float l_run;   // running sum over this lane's half of the keys
 
-    // Copy tile kt of K (to K buffer KB) and of V (to V buffer VB) into LDS;
-    // KB or VB < 0 skips that tensor.
+    // Copy tile kt of K (to K buffer KB) and/or of V (to V buffer VB) into LDS;
+    // a negative buffer index skips that tensor.  Rows past the last key lie
+    // outside the buffer range and read as zeros.
     template <int KB, int VB>
     __device__ __forceinline__ void copy_tile(int kt)
     {
-        const int key0 = kt * kBc;
-        const uint32_t soff = (uint32_t)key0 * tok_bytes;
-        if (key0 + kBc <= Skv) {
+        const uint32_t soff = (uint32_t)(kt * kBc) * tok_bytes;
 #pragma unroll
-            for (int i = 0; i < Cfg::kLoads; ++i) {
-                const int off = (i * Cfg::kWaves + wave) * 1024;
-                const uint32_t so = soff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes;
-                if constexpr (KB >= 0)
-                    copy16_to_lds(k_rsrc, kbuf[KB] + off, ld_voff, so);
-                if constexpr (VB >= 0)
-                    copy16_to_lds(v_rsrc, vbuf[VB] + off, ld_voff, so);
-            }
-        } else {
-            // partial or past-the-end tile: rows past the last key re-read the last key
-#pragma unroll
-            for (int i = 0; i < Cfg::kLoads; ++i) {
-                const int off = (i * Cfg::kWaves + wave) * 1024;
-                const int row = (wave * 64 + (int)(threadIdx.x & 63)) / Cfg::kChunks +
-                                i * Cfg::kLoadRows;
-                const int over = max(key0 + row - (Skv - 1), 0);
-                const uint32_t vo = ld_voff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes -
-                                    (uint32_t)over * tok_bytes;
-                if constexpr (KB >= 0)
-                    copy16_to_lds(k_rsrc, kbuf[KB] + off, vo, soff);
-                if constexpr (VB >= 0)
-                    copy16_to_lds(v_rsrc, vbuf[VB] + off, vo, soff);
-            }
+        for (int i = 0; i < Cfg::kLoads; ++i) {
+            const int off = (i * Cfg::kWaves + wave) * 1024;
+            const uint32_t so = soff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes;
+            if constexpr (KB >= 0)
+                copy16_to_lds(k_rsrc, kbuf[KB] + off, ld_voff, so);
+            if constexpr (VB >= 0)
+                copy16_to_lds(v_rsrc, vbuf[VB] + off, ld_voff, so);
         }
     }
 
@@ -184,7 +215,7 @@ struct FwdBf16Tile {
     template <int KB, int Q>
     __device__ __forceinline__ void read_k()
     {
-        kf[Q % 3] = as_bf16x8(ld_lds16(kbuf[KB] + k_off(Q / 2) + 32 * (Q % 2) * kRow));
+        kf[Q % 3] = ld_lds16(kbuf[KB] + k_off(Q / 2) + 32 * (Q % 2) * kRow);
     }
 
     // Transpose read E (block E/2, half E%2) of 16-key step T from V buffer VB.
@@ -201,83 +232,119 @@ struct FwdBf16Tile {
 #pragma unroll
         for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                sacc[SP][kb] = mfma32x32x16(
-                    as_bf16x8(ld_lds16(kbuf[KB] + k_off(s) + 32 * kb * kRow)), qf[s],
-                    s == 0 ? f32x16{} : sacc[SP][kb]);
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 a = ld_lds16(kbuf[KB] + k_off(s) + 32 * kb * kRow);
+                if (s == 0)
+                    mfma_s0(sacc[SP][kb], a, qf[s]);
+                else
+                    mfma_s(sacc[SP][kb], a, qf[s]);
+            }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            vgpr_wait(sacc[SP][kb]);
     }
 
-    // Softmax of the tile in sacc[P], vector work of slot I.
-    //   slots 0-3: four chains of partial maxima over 8 scores each;
-    //   slot 4:    the row maximum (both lane halves);
-    //   slot 5:    the maximum in use and this iteration's rescale factor;
-    //   slots 6..: 8 groups of 4 scores -> weights, sums, bf16 pairs;
-    //   last slot: the tile's row sum.
+    // Softmax of the tile in sacc[P], vector work of slot I:
+    //   slots 0-5:  four chains of partial maxima over 8 scores each (32-key
+    //               block kb, registers 8h..8h+7; block 0 in slots 0-3, block 1,
+    //               whose last K Q^T step ends a slot later, in slots 2-5);
+    //   slot 6:     the row maximum (both lane halves);
+    //   slot 7:     the maximum in use and this iteration's rescale factor;
+    //   slots 8..:  8 groups of 4 scores -> weights (in place), sum, bf16 pairs
+    //               (d = 128: weights of two scores per slot, then the sum and
+    //               pairs; d = 64: a group per slot).
+    static constexpr int kGroup0 = 8;
+
+    // Step STEP of the two partial-maximum chains of 32-key block KB.
+    template <int P, int KB, int STEP>
+    __device__ __forceinline__ void max_chains()
+    {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x16& s = sacc[P][KB];
+            const int o = 8 * h;
+            float& m = mxc[2 * KB + h];
+            if constexpr (STEP == 0)
+                m = fmaxf(fmaxf(s[o + 0], s[o + 1]), s[o + 2]);
+            else if constexpr (STEP == 1)
+                m = fmaxf(fmaxf(m, s[o + 3]), s[o + 4]);
+            else if constexpr (STEP == 2)
+                m = fmaxf(fmaxf(m, s[o + 5]), s[o + 6]);
+            else
+                m = fmaxf(m, s[o + 7]);
+            pin(m);
+        }
+    }
+
+    // Re-pin, right after slot I's matrix instruction, the values its vector
+    // work reads, so that work cannot be hoisted into an earlier slot.
+    template <int I>
+    __device__ __forceinline__ void slot_inputs()
+    {
+        if constexpr (I == 6) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                pin(mxc[c]);
+        } else if constexpr (I == 7) {
+            pin(m_tile);
+        } else if constexpr (I >= kGroup0 && I < kGroup0 + 8 * kPer) {
+            pin(m_used);
+        }
+    }
+
     template <int P, int I>
     __device__ __forceinline__ void softmax_part()
     {
-        constexpr int kPer = (kSlots - 8) / 8;  // slots per group of 4 scores
-        if constexpr (I < 4) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const f32x16& s = sacc[P][c / 2];
-                const int o = 8 * (c % 2);
-                if constexpr (I == 0)
-                    mxc[c] = fmaxf(fmaxf(s[o + 0], s[o + 1]), s[o + 2]);
-                else if constexpr (I == 1)
-                    mxc[c] = fmaxf(fmaxf(mxc[c], s[o + 3]), s[o + 4]);
-                else if constexpr (I == 2)
-                    mxc[c] = fmaxf(fmaxf(mxc[c], s[o + 5]), s[o + 6]);
-                else
-                    mxc[c] = fmaxf(mxc[c], s[o + 7]);
-                pin(mxc[c]);
-            }
-        } else if constexpr (I == 4) {
-            float mx = fmaxf(fmaxf(mxc[0], mxc[1]), fmaxf(mxc[2], mxc[3]));
-            mxc[0] = fmaxf(mx, partner32(mx, hh));
-            pin(mxc[0]);
-        } else if constexpr (I == 5) {
-            const float m_tile = mxc[0] * scale_log2;
+        slot_inputs<I>();
+        if constexpr (I < 4)
+            max_chains<P, 0, I>();
+        if constexpr (I >= 2 && I < 6)
+            max_chains<P, 1, I - 2>();
+        if constexpr (I == 6) {
+            const float mx = fmaxf(fmaxf(mxc[0], mxc[1]), fmaxf(mxc[2], mxc[3]));
+            m_tile = fmaxf(mx, partner32(mx, hh)) * scale_log2;
+            pin(m_tile);
+        } else if constexpr (I == 7) {
             grow = m_tile > m_used + Cfg::kRescaleThreshold;
             const float m_new = grow ? m_tile : m_used;
             alpha = exp2_fast(m_used - m_new);
             m_used = m_new;
             pin(alpha);
             pin(m_used);
-            lsum[0] = 0.f;
-            lsum[1] = 0.f;
-        } else if constexpr (I >= 6 && I < 6 + 8 * kPer) {
-            constexpr int G = (I - 6) / kPer;     // group of 4 scores
-            constexpr int sub = (I - 6) % kPer;
+            lsum = 0.f;
+        } else if constexpr (I >= kGroup0 && I < kGroup0 + 8 * kPer) {
+            constexpr int G = (I - kGroup0) / kPer;  // group of 4 scores
+            constexpr int sub = (I - kGroup0) % kPer;
             constexpr int kb = G / 4;
             constexpr int r0 = 4 * (G % 4);
             f32x16& s = sacc[P][kb];
-            if constexpr (kPer == 1) {
+            constexpr int lo = kPer == 1 ? 0 : 2 * sub, hi = kPer == 1 ? 4 : 2 * sub + 2;
+            if constexpr (kPer == 1 || sub < 2) {
 #pragma unroll
-                for (int r = r0; r < r0 + 4; ++r) {
-                    float e = exp2_fast(__builtin_fmaf(s[r], scale_log2, -m_used));
-                    pin(e);
-                    s[r] = e;
-                }
-            } else if constexpr (sub < 2) {
-#pragma unroll
-                for (int r = r0 + 2 * sub; r < r0 + 2 * sub + 2; ++r) {
+                for (int r = r0 + lo; r < r0 + hi; ++r) {
                     float e = exp2_fast(__builtin_fmaf(s[r], scale_log2, -m_used));
                     pin(e);
                     s[r] = e;
                 }
             }
             if constexpr (sub == kPer - 1) {
-                lsum[G % 2] += (s[r0] + s[r0 + 1]) + (s[r0 + 2] + s[r0 + 3]);
-                pin(lsum[G % 2]);
-                // P^T fragment t = 16-key step: registers 8(t%2)..+7 of block t/2
+                lsum += (s[r0] + s[r0 + 1]) + (s[r0 + 2] + s[r0 + 3]);
+                pin(lsum);
+                // P^T fragment of 16-key step t = registers 8(t%2)..+7 of block
+                // t/2: the even group gives its first two words, the odd group
+                // the last two
                 constexpr int t = 2 * kb + (G % 4) / 2;
-                constexpr int w = 2 * (G % 2);
-                u32x4 v = __builtin_bit_cast(u32x4, pf[P][t]);
-                v[w] = pack_bf16x2(s[r0], s[r0 + 1]);
-                v[w + 1] = pack_bf16x2(s[r0 + 2], s[r0 + 3]);
-                pin(v);
-                pf[P][t] = as_bf16x8(v);
+                if constexpr (G % 2 == 0) {
+                    pw[0] = pack_bf16x2(s[r0], s[r0 + 1]);
+                    pw[1] = pack_bf16x2(s[r0 + 2], s[r0 + 3]);
+                    pin(pw[0]);
+                    pin(pw[1]);
+                } else {
+                    u32x4 v = {pw[0], pw[1], pack_bf16x2(s[r0], s[r0 + 1]),
+                               pack_bf16x2(s[r0 + 2], s[r0 + 3])};
+                    pin(v);
+                    pf[P][t] = v;
+                }
             }
         }
     }
@@ -294,11 +361,14 @@ struct FwdBf16Tile {
         constexpr int v = I / 2;
         if constexpr (I % 2 == 0) {
             constexpr int t = v / kMB, mb = v % kMB;
-            oacc[mb] = mfma32x32x16(cat_bf16x8(vf[2 * mb], vf[2 * mb + 1]), pf[P ^ 1][t],
-                                    oacc[mb]);
+            mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
+                   pf[P ^ 1][t]);
         } else {
             constexpr int s = v / 2, kb = v % 2;
-            sacc[P ^ 1][kb] = mfma32x32x16(kf[v % 3], qf[s], s == 0 ? f32x16{} : sacc[P ^ 1][kb]);
+            if constexpr (s == 0)
+                mfma_s0(sacc[P ^ 1][kb], kf[v % 3], qf[s]);
+            else
+                mfma_s(sacc[P ^ 1][kb], kf[v % 3], qf[s]);
             if constexpr (v + 2 < 2 * kSteps)
                 read_k<P ^ 1, v + 2>();
         }
@@ -333,6 +403,9 @@ struct FwdBf16Tile {
         if (key0 + kBc > Skv) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
+                vgpr_wait(sacc[P][kb]);  // the last K Q^T steps may still run
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = key0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
@@ -348,30 +421,17 @@ struct FwdBf16Tile {
         read_k<P ^ 1, 1>();
         __builtin_amdgcn_sched_barrier(0);
         slots<P, 0>();
-        l_run = __builtin_fmaf(l_run, alpha, lsum[0] + lsum[1]);
+        l_run = __builtin_fmaf(l_run, alpha, lsum);
         if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-            for (int mb = 0; mb < kMB; ++mb)
+            for (int mb = 0; mb < kMB; ++mb) {
+                acc_wait(oacc[mb]);
                 oacc[mb] *= alpha;
+                acc_wait(oacc[mb]);
+            }
         }
         wait_vmem_all();
         __syncthreads();
-    }
-
-    // P V of the last tile (parity P), after the loop.
-    template <int P>
-    __device__ __forceinline__ void last_pv()
-    {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            u32x2 f[kVReads];
-#pragma unroll
-            for (int e = 0; e < kVReads; ++e)
-                f[e] = ld_lds_tr16(vbuf[P] + v_addr[e] + 16 * t * kRow);
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb)
-                oacc[mb] = mfma32x32x16(cat_bf16x8(f[2 * mb], f[2 * mb + 1]), pf[P][t], oacc[mb]);
-        }
     }
 };
 
@@ -440,12 +500,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         const uint16_t* src = Q + ((long)b * Sq * H + h) * D + (long)q_row * tok + 8 * hh;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            st.qf[s] = as_bf16x8(ld_global16(src + 16 * s));
+            st.qf[s] = ld_global16(src + 16 * s);
     } else {
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-            st.qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+            st.qf[s] = u32x4{0, 0, 0, 0};
     }
+
+    // Q^T lives in accumulation registers for the whole kernel (the K Q^T asm
+    // takes B from there); moving it once here keeps the compiler from copying
+    // it over before every matrix instruction.
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+        asm volatile("" : "+a"(st.qf[s]));
 
     // Per-lane LDS bases.  K operand (A of S^T), step s: row n (+32 for the
     // second block), column 16s + 8hh.  V transpose reads, block mb, half hi:
@@ -465,11 +532,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
                 st.v_addr[2 * mb + hi] = lds_byte<D>(vr + 8 * hi, 32 * mb + vc);
     }
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+    for (int mb = 0; mb < kMB; ++mb) {
         st.oacc[mb] = f32x16{};
+        acc_wait(st.oacc[mb]);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        st.pf[1][t] = as_bf16x8(u32x4{0, 0, 0, 0});
+        st.pf[1][t] = u32x4{0, 0, 0, 0};
     st.m_used = -INFINITY;
     st.l_run = 0.f;
 
@@ -478,17 +547,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     st.template qk_tile<0, 0>();
     __syncthreads();  // K buffer 0 is refilled by the first iteration
 
-    int kt = 0;
-    for (; kt + 1 < st.n_kt; kt += 2) {
+    // Iterations run in pairs (the buffer index is compile-time); the ones past
+    // the last tile see only keys >= Skv, so their weights are 0, and the
+    // first of them accumulates the last tile's P V.
+    const int n_it = (st.n_kt + 2) & ~1;
+    for (int kt = 0; kt < n_it; kt += 2) {
         st.template iteration<0>(kt);
         st.template iteration<1>(kt + 1);
     }
-    if (kt < st.n_kt) {
-        st.template iteration<0>(kt);
-        st.template last_pv<0>();
-    } else {
-        st.template last_pv<1>();
-    }
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+        acc_wait(st.oacc[mb]);
 
     const float l_tot = st.l_run + partner32(st.l_run, hh);
     const float inv_l = 1.f / l_tot;
