@@ -24,6 +24,7 @@ DIT_ERR_ALIGN = 4
 DIT_ERR_VALUE = 5
 DIT_ERR_ALIAS = 6
 DIT_ERR_HIP = 7
+DIT_ERR_WORKSPACE = 8
 
 DIT_DTYPE_BF16 = 0
 DIT_DTYPE_FP8_E4M3 = 1
@@ -61,6 +62,10 @@ def load():
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.dit_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.dit_attn_fwd.restype = I
+    lib.dit_attn_fwd_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.dit_attn_fwd_workspace_size.restype = I
+    lib.dit_attn_fwd_ws.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
+    lib.dit_attn_fwd_ws.restype = I
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, P]
     lib.dit_attn_merge.restype = I
     lib.dit_quant_fp8.argtypes = [P, P, P, I, I, I, I, P]
@@ -139,6 +144,38 @@ def dit_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,
     ``fp8_tensor(data, scale)`` descriptors.  o: bf16 [B,Sq,H,d]; lse: fp32
     [B,H,Sq].  stream: None = torch's current stream, 0 = the null stream."""
     _check(dit_attn_fwd_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, stream))
+
+
+def dit_attn_fwd_workspace_size_status(B, H, Sq, Skv, d, dtype=DIT_DTYPE_BF16):
+    """Call dit_attn_fwd_workspace_size: returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = load().dit_attn_fwd_workspace_size(int(B), int(H), int(Sq), int(Skv), int(d),
+                                            int(dtype), ctypes.byref(n))
+    return st, n.value
+
+
+def dit_attn_fwd_workspace_size(B, H, Sq, Skv, d, dtype=DIT_DTYPE_BF16) -> int:
+    """Bytes of workspace dit_attn_fwd_ws needs for this shape on the current device."""
+    st, n = dit_attn_fwd_workspace_size_status(B, H, Sq, Skv, d, dtype)
+    _check(st)
+    return n
+
+
+def dit_attn_fwd_ws_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,
+                           workspace=None, workspace_bytes=0, stream=None) -> int:
+    """Call dit_attn_fwd_ws and return its status code (no exception)."""
+    args = [_fwd_operand(t, dtype) for t in (q, k, v)]
+    return load().dit_attn_fwd_ws(args[0], args[1], args[2], _addr(o), _addr(lse), int(B),
+                                  int(H), int(Sq), int(Skv), int(d), float(scale), int(dtype),
+                                  _addr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def dit_attn_fwd_ws(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,
+                    workspace=None, workspace_bytes=0, stream=None) -> None:
+    """dit_attn_fwd with caller-provided scratch (see the header): the last wave
+    of workgroups is split over the keys and merged."""
+    _check(dit_attn_fwd_ws_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, workspace,
+                                  workspace_bytes, stream))
 
 
 def dit_attn_merge_status(o_parts, lse_parts, n_parts, o, lse, B, H, Sq, d, stream=None) -> int:

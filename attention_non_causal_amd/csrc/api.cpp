@@ -81,13 +81,50 @@ const char* dit_status_string(int status)
         return "an output overlaps an input";
     case DIT_ERR_HIP:
         return "HIP kernel launch failed";
+    case DIT_ERR_WORKSPACE:
+        return "workspace missing, too small, misaligned or overlapping a tensor";
     default:
         return "unknown status";
     }
 }
 
-int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int Sq, int Skv, int d, float scale, int dtype, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Compute units of the current device (the split plan depends on them).
+int current_cu_count(int* n_cu)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return DIT_ERR_HIP;
+    return DIT_OK;
+}
+
+// Shape checks shared by the forward entry points.
+int check_fwd_shape(int B, int H, int Sq, int Skv, int d, int dtype)
+{
+    if (dtype != DIT_DTYPE_BF16 && dtype != DIT_DTYPE_FP8_E4M3)
+        return DIT_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128)
+        return DIT_ERR_UNSUPPORTED;
+    const int64_t esz = dtype == DIT_DTYPE_BF16 ? 2 : 1;
+    const int64_t q_bytes = checked_bytes({B, Sq, H, d, esz});
+    const int64_t kv_bytes = checked_bytes({B, Skv, H, d, esz});
+    const int64_t o_bytes = checked_bytes({B, Sq, H, d, 2});
+    const int64_t lse_bytes = checked_bytes({B, H, Sq, 4});
+    if (q_bytes < 0 || kv_bytes < 0 || o_bytes < 0 || lse_bytes < 0)
+        return DIT_ERR_SHAPE;
+    if (kv_bytes / B > kMaxKvBytesPerBatch)
+        return DIT_ERR_SHAPE;
+    return DIT_OK;
+}
+
+// dit_attn_fwd and dit_attn_fwd_ws; with_ws selects the split launch.
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int Sq, int Skv, int d, float scale, int dtype, bool with_ws, void* ws,
+             size_t ws_bytes, hipStream_t stream)
 {
     if (!q || !k || !v || !o || !lse)
         return DIT_ERR_NULL;
@@ -159,9 +196,65 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     a.Skv = Skv;
     a.d = d;
     a.scale = scale;
-    if (dtype == DIT_DTYPE_BF16)
-        return map_hip(dit::launch_fwd_bf16(a, stream));
-    return map_hip(dit::launch_fwd_fp8(a, stream));
+    if (dtype != DIT_DTYPE_BF16)
+        return map_hip(dit::launch_fwd_fp8(a, stream));
+
+    dit::FwdSplit split = {};
+    if (with_ws) {
+        int n_cu = 0;
+        const int st = current_cu_count(&n_cu);
+        if (st != DIT_OK)
+            return st;
+        split = dit::plan_fwd_bf16_split(B, H, Sq, Skv, d, n_cu);
+        if (split.n_tail > 0) {
+            if (!ws || ws_bytes < split.ws_bytes || !aligned(ws, 16))
+                return DIT_ERR_WORKSPACE;
+            const Range rw = range(ws, (int64_t)split.ws_bytes);
+            for (const Range& in : inputs)
+                if (overlap(rw, in))
+                    return DIT_ERR_WORKSPACE;
+            if (overlap(rw, ro) || overlap(rw, rl))
+                return DIT_ERR_WORKSPACE;
+            a.ws = ws;
+        }
+    }
+    return map_hip(dit::launch_fwd_bf16(a, split, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Sq, int Skv, int d, float scale, int dtype, hipStream_t stream)
+{
+    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, false, nullptr, 0, stream);
+}
+
+int dit_attn_fwd_workspace_size(int B, int H, int Sq, int Skv, int d, int dtype, size_t* bytes)
+{
+    if (!bytes)
+        return DIT_ERR_NULL;
+    const int st = check_fwd_shape(B, H, Sq, Skv, d, dtype);
+    if (st != DIT_OK)
+        return st;
+    *bytes = 0;
+    if (dtype != DIT_DTYPE_BF16)
+        return DIT_OK;
+    int n_cu = 0;
+    const int hs = current_cu_count(&n_cu);
+    if (hs != DIT_OK)
+        return hs;
+    *bytes = dit::plan_fwd_bf16_split(B, H, Sq, Skv, d, n_cu).ws_bytes;
+    return DIT_OK;
+}
+
+int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int Sq, int Skv, int d, float scale, int dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream)
+{
+    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
+                    workspace_bytes, stream);
 }
 
 int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, int n_parts,

@@ -53,6 +53,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace dit {
 namespace {
 
@@ -166,7 +168,7 @@ struct FwdBf16Tile {
     uint8_t* vbuf[2];
     __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
     uint32_t tok_bytes;
-    int Skv, n_kt, wave, hh;
+    int key_end, wave, hh;   // keys >= key_end are masked (the end of this block's range)
     float scale_log2;
     uint32_t ld_voff;        // this lane's offset in copy 0 (copy i: + i * kLoadRows rows)
     u32x4 qf[kSteps];        // bf16 operands are carried as raw 32-bit words
@@ -400,7 +402,7 @@ struct FwdBf16Tile {
         copy_tile<-1, P>(kt);
         copy_tile<P, -1>(kt + 2);
         const int key0 = kt * kBc;
-        if (key0 + kBc > Skv) {
+        if (key0 + kBc > key_end) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 vgpr_wait(sacc[P][kb]);  // the last K Q^T steps may still run
@@ -409,7 +411,7 @@ struct FwdBf16Tile {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = key0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-                    if (key >= Skv)
+                    if (key >= key_end)
                         sacc[P][kb][r] = -INFINITY;
                 }
         }
@@ -435,11 +437,19 @@ struct FwdBf16Tile {
     }
 };
 
+// Grid: blocks [0, n_main) each take one query tile over all keys; the
+// remaining query tiles (the last, partial wave of workgroups a plain launch
+// would end with) are each split into nsplit pieces over contiguous ranges of
+// key tiles, so they fill the machine instead of leaving most of it idle.  A
+// piece writes its normalised fp32 partial O and its LSE to the workspace
+// (ws_o [piece][kBr][D], ws_lse [piece][kBr]); split_merge_kernel combines
+// them with the log-sum-exp merge.
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int H, int Sq, int Skv, float scale_log2, int n_qtiles, int n_blocks)
+    int H, int Sq, int Skv, float scale_log2, int n_qtiles, int n_main, int nsplit,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse)
 {
     using Cfg = FwdBf16Cfg<D>;
     constexpr int kMB = Cfg::kMB;
@@ -454,7 +464,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const int n = lane & 31;   // query column of this lane within the wave
     const int hh = lane >> 5;  // which 8-wide k group this lane feeds
 
-    const int logical = xcd_remap(blockIdx.x, n_blocks);
+    const int n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
+    int logical, kt0, kt1, piece;
+    if ((int)blockIdx.x < n_main) {
+        logical = xcd_remap(blockIdx.x, n_main);
+        kt0 = 0;
+        kt1 = n_kt;
+        piece = -1;
+    } else {
+        piece = blockIdx.x - n_main;
+        logical = n_main + piece / nsplit;
+        const int part = piece % nsplit;
+        kt0 = (int)((long)part * n_kt / nsplit);
+        kt1 = (int)((long)(part + 1) * n_kt / nsplit);
+    }
     const int qt = logical % n_qtiles;
     const int bh = logical / n_qtiles;
     const int h = bh % H;
@@ -468,8 +491,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     st.vbuf[1] = v_lds1;
     st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     st.hh = hh;
-    st.Skv = Skv;
-    st.n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
+    st.key_end = min(kt1 * Cfg::kBc, Skv);
     st.scale_log2 = scale_log2;
     st.tok_bytes = (uint32_t)(tok * 2);
     {
@@ -490,10 +512,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         const int r = p / Cfg::kChunks;
         st.ld_voff = (uint32_t)r * st.tok_bytes + swz_slot<D>(r, p % Cfg::kChunks) * 16;
     }
-    // K(0), K(1) for the first two K Q^T products; V(1) into V buffer 1, where
-    // the first iteration's P V (with P = 0) reads finite values.
-    st.template copy_tile<0, -1>(0);
-    st.template copy_tile<1, 1>(1);
+    // K(kt0), K(kt0+1) for the first two K Q^T products; V(kt0+1) into V buffer
+    // 1, where the first iteration's P V (with P = 0) reads finite values.
+    st.template copy_tile<0, -1>(kt0);
+    st.template copy_tile<1, 1>(kt0 + 1);
 
     const int q_row = qt * Cfg::kBr + st.wave * 32 + n;
     if (q_row < Sq) {
@@ -548,12 +570,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     __syncthreads();  // K buffer 0 is refilled by the first iteration
 
     // Iterations run in pairs (the buffer index is compile-time); the ones past
-    // the last tile see only keys >= Skv, so their weights are 0, and the
-    // first of them accumulates the last tile's P V.
-    const int n_it = (st.n_kt + 2) & ~1;
-    for (int kt = 0; kt < n_it; kt += 2) {
-        st.template iteration<0>(kt);
-        st.template iteration<1>(kt + 1);
+    // the last tile of the range see only masked keys, so their weights are 0,
+    // and the first of them accumulates the last tile's P V.
+    const int n_it = (kt1 - kt0 + 2) & ~1;
+    for (int i = 0; i < n_it; i += 2) {
+        st.template iteration<0>(kt0 + i);
+        st.template iteration<1>(kt0 + i + 1);
     }
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
@@ -561,7 +583,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
     const float l_tot = st.l_run + partner32(st.l_run, hh);
     const float inv_l = 1.f / l_tot;
-    if (q_row < Sq) {
+    if (piece >= 0) {
+        // partial result of a split tile: normalised fp32 O and LSE (natural log)
+        const int r = st.wave * 32 + n;
+        float* dst = ws_o + ((long)piece * Cfg::kBr + r) * D + 4 * hh;
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 w = {st.oacc[mb][4 * g + 0] * inv_l, st.oacc[mb][4 * g + 1] * inv_l,
+                           st.oacc[mb][4 * g + 2] * inv_l, st.oacc[mb][4 * g + 3] * inv_l};
+                *reinterpret_cast<f32x4*>(dst + 32 * mb + 8 * g) = w;
+            }
+        if (hh == 0)
+            ws_lse[(long)piece * Cfg::kBr + r] = (st.m_used + log2_fast(l_tot)) * kLn2;
+    } else if (q_row < Sq) {
         uint16_t* dst = O + ((long)b * Sq * H + h) * D + (long)q_row * tok + 4 * hh;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
@@ -577,8 +613,81 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
 }
 
+// Combine the nsplit partial results of each split query tile:
+//     M = max_p LSE_p,  w_p = exp(LSE_p - M),
+//     O = sum_p w_p O_p / sum_p w_p,  LSE = M + ln sum_p w_p.
+// One thread per (split tile, row, 4 channels).
 template <int D>
-hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t stream)
+__global__ __launch_bounds__(256) void split_merge_kernel(
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, int H, int Sq, int n_qtiles, int n_main, int nsplit, int n_tail)
+{
+    constexpr int kBr = FwdBf16Cfg<D>::kBr;
+    constexpr int kChunks = D / 4;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)n_tail * kBr * kChunks)
+        return;
+    const int c = (int)(idx % kChunks);
+    const int r = (int)((idx / kChunks) % kBr);
+    const int t = (int)(idx / ((long)kChunks * kBr));
+    const int tile = n_main + t;
+    const int qt = tile % n_qtiles;
+    const int bh = tile / n_qtiles;
+    const int h = bh % H;
+    const int b = bh / H;
+    const int q_row = qt * kBr + r;
+    if (q_row >= Sq)
+        return;
+    const long p0 = (long)t * nsplit;
+    float m = -INFINITY;
+    for (int p = 0; p < nsplit; ++p)
+        m = fmaxf(m, ws_lse[(p0 + p) * kBr + r]);
+    float wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < nsplit; ++p) {
+        const float w = exp2_fast((ws_lse[(p0 + p) * kBr + r] - m) * kLog2e);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(ws_o + ((p0 + p) * kBr + r) * D + 4 * c);
+        acc += w * o;
+        wsum += w;
+    }
+    const float inv = 1.f / wsum;
+    u32x2 out;
+    out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(O + (((long)b * Sq + q_row) * H + h) * D + 4 * c) = out;
+    if (c == 0)
+        LSE[((long)b * H + h) * Sq + q_row] = m + log2_fast(wsum) * kLn2;
+}
+
+template <int D>
+FwdSplit plan_d(int B, int H, int Sq, int Skv, int n_cu)
+{
+    using Cfg = FwdBf16Cfg<D>;
+    FwdSplit sp = {};
+    const long n_qtiles = (Sq + Cfg::kBr - 1) / Cfg::kBr;
+    const long n_blocks = n_qtiles * H * B;
+    const long n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
+    const long slots = 2L * n_cu;  // two workgroups per CU
+    sp.n_main = (int)n_blocks;
+    sp.nsplit = 1;
+    if (n_cu <= 0 || n_blocks > 0x7fffffffL)
+        return sp;
+    const long rem = n_blocks % slots;
+    // split only a last wave that would leave at least half of the machine idle,
+    // into pieces of at least 4 key tiles
+    long nsplit = rem > 0 ? slots / rem : 0;
+    nsplit = std::min({nsplit, n_kt / 4, (long)kMaxSplit});
+    if (rem == 0 || 2 * rem > slots || nsplit < 2)
+        return sp;
+    sp.n_main = (int)(n_blocks - rem);
+    sp.nsplit = (int)nsplit;
+    sp.n_tail = (int)rem;
+    sp.ws_bytes = (size_t)(rem * nsplit) * Cfg::kBr * (D + 1) * sizeof(float);
+    return sp;
+}
+
+template <int D>
+hipError_t launch_fwd_bf16_d(const FwdArgs& a, const FwdSplit& sp, hipStream_t stream)
 {
     using Cfg = FwdBf16Cfg<D>;
     const int n_qtiles = (a.Sq + Cfg::kBr - 1) / Cfg::kBr;
@@ -586,16 +695,34 @@ hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t stream)
     if (n_blocks > 0x7fffffffL)
         return hipErrorInvalidConfiguration;
     const float scale_log2 = a.scale * kLog2e;
-    return launch_kernel(fwd_bf16_kernel<D>, dim3((unsigned)n_blocks), dim3(Cfg::kThreads),
-                         stream, a.q, a.k, a.v, a.o, a.lse, a.H, a.Sq, a.Skv, scale_log2,
-                         n_qtiles, (int)n_blocks);
+    const bool split = sp.n_tail > 0;
+    float* ws_o = split ? static_cast<float*>(a.ws) : nullptr;
+    float* ws_lse = split ? ws_o + (size_t)sp.n_tail * sp.nsplit * Cfg::kBr * D : nullptr;
+    const long grid = split ? (long)sp.n_main + (long)sp.n_tail * sp.nsplit : n_blocks;
+    hipError_t e = launch_kernel(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(Cfg::kThreads),
+                                 stream, a.q, a.k, a.v, a.o, a.lse, a.H, a.Sq, a.Skv, scale_log2,
+                                 n_qtiles, split ? sp.n_main : (int)n_blocks,
+                                 split ? sp.nsplit : 1, ws_o, ws_lse);
+    if (e != hipSuccess || !split)
+        return e;
+    const long n_threads = (long)sp.n_tail * Cfg::kBr * (D / 4);
+    return launch_kernel(split_merge_kernel<D>, dim3((unsigned)((n_threads + 255) / 256)),
+                         dim3(256), stream, (const float*)ws_o, (const float*)ws_lse,
+                         static_cast<uint16_t*>(a.o), a.lse, a.H, a.Sq, n_qtiles, sp.n_main,
+                         sp.nsplit, sp.n_tail);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream)
+FwdSplit plan_fwd_bf16_split(int B, int H, int Sq, int Skv, int d, int n_cu)
 {
-    return a.d == 64 ? launch_fwd_bf16_d<64>(a, stream) : launch_fwd_bf16_d<128>(a, stream);
+    return d == 64 ? plan_d<64>(B, H, Sq, Skv, n_cu) : plan_d<128>(B, H, Sq, Skv, n_cu);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdSplit& split, hipStream_t stream)
+{
+    return a.d == 64 ? launch_fwd_bf16_d<64>(a, split, stream)
+                     : launch_fwd_bf16_d<128>(a, split, stream);
 }
 
 }  // namespace dit

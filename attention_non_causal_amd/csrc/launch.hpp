@@ -17,6 +17,18 @@ struct FwdArgs {
     float* lse;            // fp32 [B][H][Sq]
     int B, H, Sq, Skv, d;
     float scale;
+    void* ws;              // bf16 path: workspace of the split launch (see FwdSplit)
+};
+
+// Split plan of the bf16 forward pass (fwd_bf16.hip): the first n_main query
+// tiles run over all keys, the last n_tail are split into nsplit pieces over
+// the keys, whose partial results need ws_bytes of workspace (n_tail == 0: no
+// split, no workspace).
+constexpr int kMaxSplit = 16;
+
+struct FwdSplit {
+    int n_main, nsplit, n_tail;
+    size_t ws_bytes;
 };
 
 constexpr int kMaxMergeParts = 16;
@@ -30,7 +42,8 @@ struct MergeArgs {
     int B, H, Sq, d;
 };
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+FwdSplit plan_fwd_bf16_split(int B, int H, int Sq, int Skv, int d, int n_cu);
+hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdSplit& split, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8(const void* x, void* x8, float* scale, int B, int H, int S, int d,

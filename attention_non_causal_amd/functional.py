@@ -20,8 +20,23 @@ def _require(t, dtype, name):
         raise ValueError(f"{name} must be contiguous [B,S,H,d]")
 
 
-def attention(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
-    """bf16 non-causal attention: returns (o bf16 [B,Sq,H,d], lse fp32 [B,H,Sq])."""
+def workspace_for(q, k, dtype=None):
+    """A workspace tensor for dit_attn_fwd_ws on q's shape (None if none is needed)."""
+    import torch
+    B, Sq, H, d = q.shape
+    Skv = k.shape[1]
+    dt = _lib.DIT_DTYPE_BF16 if dtype is None else dtype
+    n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d, dt)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def attention(q, k, v, scale: float | None = None, out=None, lse=None, stream=None,
+              workspace="auto"):
+    """bf16 non-causal attention: returns (o bf16 [B,Sq,H,d], lse fp32 [B,H,Sq]).
+
+    workspace: "auto" (default) allocates the scratch dit_attn_fwd_ws needs and
+    balances the last wave of workgroups; a uint8 device tensor is used as that
+    scratch; None calls dit_attn_fwd (no scratch, no split)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, torch.bfloat16, n)
@@ -33,7 +48,17 @@ def attention(q, k, v, scale: float | None = None, out=None, lse=None, stream=No
         out = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    _lib.dit_attn_fwd(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16, stream)
+    if workspace is None:
+        _lib.dit_attn_fwd(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                          stream)
+        return out, lse
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        workspace = workspace_for(q, k)
+    n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.dit_attn_fwd_ws(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                         workspace, n_bytes, stream)
     return out, lse
 
 

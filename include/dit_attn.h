@@ -44,12 +44,13 @@
 #define DIT_ATTN_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define DIT_ATTN_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define DIT_ATTN_VERSION 10100 /* major*10000 + minor*100 + patch */
 
 enum dit_status {
     DIT_OK = 0,
@@ -60,7 +61,10 @@ enum dit_status {
     DIT_ERR_ALIGN = 4,       /* tensor not 16-byte aligned (LSE/scales: 4-byte)    */
     DIT_ERR_VALUE = 5,       /* scale not finite or not > 0                        */
     DIT_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap     */
-    DIT_ERR_HIP = 7          /* the HIP launch reported an error                   */
+    DIT_ERR_HIP = 7,         /* the HIP launch (or device query) reported an error */
+    DIT_ERR_WORKSPACE = 8    /* dit_attn_fwd_ws: workspace NULL, smaller than
+                                dit_attn_fwd_workspace_size, not 16-byte aligned,
+                                or overlapping a tensor                            */
 };
 
 enum dit_dtype {
@@ -99,6 +103,38 @@ typedef struct dit_fp8_tensor {
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int Sq, int Skv, int d, float scale, int dtype,
                  hipStream_t stream);
+
+/*
+ * dit_attn_fwd_workspace_size / dit_attn_fwd_ws -- the bf16 forward pass with
+ * caller-provided scratch, used to balance the last wave of workgroups.
+ *
+ * A launch of dit_attn_fwd runs one workgroup per 128-query tile; when the
+ * number of tiles is not a multiple of what the GPU runs at once (two per
+ * compute unit), the last wave leaves most of the GPU idle.  dit_attn_fwd_ws
+ * runs the leftover tiles split over contiguous ranges of the keys instead
+ * (the ring dimension of "xDiT 项目概述" sec. 3.2 applied inside one GPU),
+ * writes their partial O and LSE to the workspace and combines them with the
+ * log-sum-exp merge (as dit_attn_merge does).  Results equal dit_attn_fwd's
+ * up to fp32 rounding order.
+ *
+ * dit_attn_fwd_workspace_size: *bytes = the workspace the call needs for this
+ *   shape on the current HIP device (0 if nothing is split: then workspace may
+ *   be NULL).  Shape arguments as for dit_attn_fwd; needs a HIP device
+ *   (DIT_ERR_HIP if the device query fails).
+ * dit_attn_fwd_ws: arguments as dit_attn_fwd, plus
+ *   workspace: device memory of workspace_bytes bytes, 16-byte aligned, owned
+ *   by the caller, not overlapping any tensor; its contents on entry do not
+ *   matter and on return are unspecified.  Calls that may run concurrently
+ *   need separate workspaces.  With dtype DIT_DTYPE_FP8_E4M3 the workspace is
+ *   not used (size 0) and the call equals dit_attn_fwd.
+ *   Errors as dit_attn_fwd, plus DIT_ERR_WORKSPACE.  The required size is
+ *   checked against the current device after the other arguments.
+ */
+int dit_attn_fwd_workspace_size(int B, int H, int Sq, int Skv, int d, int dtype, size_t* bytes);
+
+int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Sq, int Skv, int d, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dit_attn_merge -- combine n partial attention results over disjoint key

@@ -24,8 +24,9 @@ def fwd(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
 
 def test_library_exports_header_functions():
     names = _lib.header_functions()
-    assert set(names) == {"dit_attn_fwd", "dit_attn_merge", "dit_quant_fp8",
-                          "dit_status_string", "dit_version"}
+    assert set(names) == {"dit_attn_fwd", "dit_attn_fwd_workspace_size", "dit_attn_fwd_ws",
+                          "dit_attn_merge", "dit_quant_fp8", "dit_status_string",
+                          "dit_version"}
     lib = _lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -36,9 +37,9 @@ def test_library_exports_header_functions():
 
 
 def test_version_and_status_strings():
-    assert _lib.dit_version() == 10000
-    texts = [_lib.dit_status_string(s) for s in range(8)]
-    assert len(set(texts)) == 8 and all(texts)
+    assert _lib.dit_version() == 10100
+    texts = [_lib.dit_status_string(s) for s in range(9)]
+    assert len(set(texts)) == 9 and all(texts)
     assert _lib.dit_status_string(99) == "unknown status"
     assert _lib.dit_status_string(-1) == "unknown status"
 
@@ -141,3 +142,40 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(_lib.LibraryNotBuilt):
         _lib.dit_version()
+
+
+# ------------------------------------------------- workspace entry points
+
+def fwd_ws(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
+           dtype=DIT_DTYPE_BF16, ws=None, ws_bytes=0):
+    return _lib.dit_attn_fwd_ws_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, ws,
+                                       ws_bytes, stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), DIT_ERR_NULL), (dict(lse=None), DIT_ERR_NULL),
+    (dict(dtype=2), DIT_ERR_UNSUPPORTED), (dict(d=96), DIT_ERR_UNSUPPORTED),
+    (dict(B=0), DIT_ERR_SHAPE), (dict(H=64, Skv=1 << 18, d=128), DIT_ERR_SHAPE),
+    (dict(scale=math.nan), DIT_ERR_VALUE), (dict(o=O + 8), DIT_ERR_ALIGN),
+    (dict(o=Q), DIT_ERR_ALIAS),
+])
+def test_fwd_ws_rejects_like_fwd(kw, status):
+    """The workspace entry point validates its tensor arguments exactly as
+    dit_attn_fwd does, before any HIP call."""
+    assert fwd_ws(**kw) == status
+    assert fwd(**kw) == status
+
+
+def test_workspace_size_argument_checks():
+    st, _ = _lib.dit_attn_fwd_workspace_size_status(1, 2, 256, 256, 64)
+    assert st in (_lib.DIT_OK, _lib.DIT_ERR_HIP)  # DIT_ERR_HIP: no HIP device here
+    lib = _lib.load()
+    assert lib.dit_attn_fwd_workspace_size(1, 2, 256, 256, 64, DIT_DTYPE_BF16, None) == DIT_ERR_NULL
+    for args, status in [((0, 2, 256, 256, 64, 0), DIT_ERR_SHAPE),
+                         ((1, 2, 256, 256, 96, 0), DIT_ERR_UNSUPPORTED),
+                         ((1, 2, 256, 256, 64, 5), DIT_ERR_UNSUPPORTED),
+                         ((1, 64, 256, 1 << 18, 128, 0), DIT_ERR_SHAPE)]:
+        assert _lib.dit_attn_fwd_workspace_size_status(*args)[0] == status
+    # the fp8 path never uses a workspace and needs no device to say so
+    assert _lib.dit_attn_fwd_workspace_size_status(1, 2, 256, 256, 64, DIT_DTYPE_FP8_E4M3) == \
+        (_lib.DIT_OK, 0)
