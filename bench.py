@@ -2,9 +2,11 @@
 
 Headline: attention TFLOP/s (4*B*H*Sq*Skv*d / time) of the bf16 forward pass on
 the FLUX-like workload (B1 H24 S16896 d128), with inputs already resident in
-HBM.  A step is one dit_attn_fwd launch over the whole workload.  The kernel's
-average launch duration is measured with HIP events on the stream it runs on,
-and compared with MI355X's dense bf16 MFMA peak (2.5 PFLOP/s).  The fp64 CPU
+HBM.  A step is one dit_attn_fwd_ws call over the whole workload: the forward
+kernel, whose last partial wave of query tiles is split over the keys, and the
+small kernel that merges those pieces (workspace allocated once, before timing).
+The step's average duration is measured with HIP events on the stream it runs
+on, and compared with MI355X's dense bf16 MFMA peak (2.5 PFLOP/s).  The fp64 CPU
 oracle is timed on a bounded sample of the same workload (cpu_baseline).
 
 Extra lines of the hot path (fp8 forward with its quantiser, the SD3-like and
@@ -67,6 +69,24 @@ def time_launches(fn, steps, warmup):
     return wall, [a.elapsed_time(b) for a, b in ev]
 
 
+def time_batched(fn, steps, warmup):
+    """ms per call of a short launch: one event pair around `steps` back-to-back
+    calls on torch's current stream (per-call event pairs would mostly measure
+    launch gaps for kernels of a few tens of microseconds)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def cpu_baseline(W, g, budget_s):
     """Time the fp64 oracle on a bounded sample of query rows (all heads, all
     keys) of the same workload; report its TFLOP/s."""
@@ -120,8 +140,9 @@ def bench_fwd(W, g, dev, steps, warmup):
     q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)
     o = torch.empty_like(q)
     lse = torch.empty((W.B, W.H, W.Sq), dtype=torch.float32, device=dev)
-    wall, evs = time_launches(lambda: F.attention(q, k, v, W.scale, out=o, lse=lse), steps,
-                              warmup)
+    ws = F.workspace_for(q, k)  # scratch of the split launch, allocated before timing
+    wall, evs = time_launches(lambda: F.attention(q, k, v, W.scale, out=o, lse=lse, workspace=ws),
+                              steps, warmup)
     return wall, evs
 
 
@@ -198,7 +219,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(), "traffic_unit": "bytes/launch",
                      "algorithmic_bytes": W.algorithmic_bytes,
-                     "kernel": "fwd_bf16_kernel<128>", "kernel_ms": round(kern_ms, 4)},
+                     "kernel": "fwd_bf16_kernel<128> (+ split_merge_kernel<128>, a few us)",
+                     "kernel_ms": round(kern_ms, 4)},
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "extras": extras,
@@ -215,8 +237,12 @@ def run_extras(dev, steps, warmup):
     for name in ("tiny", "sd3"):
         W = wl.WORKLOADS[name]
         g = wl.generate(W)
-        wall, evs = bench_fwd(W, g, dev, steps, warmup)
-        ms = float(np.mean(evs))
+        q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((W.B, W.H, W.Sq), dtype=torch.float32, device=dev)
+        ws = F.workspace_for(q, k)
+        ms = time_batched(lambda: F.attention(q, k, v, W.scale, out=o, lse=lse, workspace=ws),
+                          4 * steps, warmup)
         res[name] = {"kernel_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1)}
         log(f"extra {name}: {ms:.3f} ms, {res[name]['tflops']} TFLOP/s")
 
@@ -233,8 +259,7 @@ def run_extras(dev, steps, warmup):
         lambda: F.ring_share_attention(q, k, v, W.n_chunks, W.scale, parts=parts, out=o, lse=lse),
         steps, warmup)
     ms = float(np.mean(evs))
-    _, mevs = time_launches(lambda: F.merge(parts[0], parts[1], out=o, lse=lse), steps, warmup)
-    mms = float(np.mean(mevs))
+    mms = time_batched(lambda: F.merge(parts[0], parts[1], out=o, lse=lse), 4 * steps, warmup)
     merge_bytes = W.n_chunks * (W.Sq * W.H * W.d * 2 + W.H * W.Sq * 4) + W.Sq * W.H * W.d * 2 \
         + W.H * W.Sq * 4
     res["wan_ring"] = {"total_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1),
@@ -267,9 +292,8 @@ def run_extras(dev, steps, warmup):
                         bufs["v"][1], W.scale, out=o, lse=lse)
 
     quant_all()
-    _, qevs = time_launches(lambda: _lib.dit_quant_fp8(k, bufs["k"][0], bufs["k"][1], W.B, W.H,
-                                                       W.Skv, W.d), steps, warmup)
-    qms = float(np.mean(qevs))
+    qms = time_batched(lambda: _lib.dit_quant_fp8(k, bufs["k"][0], bufs["k"][1], W.B, W.H,
+                                                   W.Skv, W.d), 4 * steps, warmup)
     qbytes = W.B * W.Skv * W.H * W.d * 3 + nblk * W.B * W.H * 4
     res["quant_fp8"] = {"kernel_ms": round(qms, 4), "GBs": round(qbytes / qms / 1e6, 1)}
     log(f"extra quant_fp8 (one tensor): {qms:.4f} ms = {res['quant_fp8']['GBs']} GB/s")
