@@ -101,6 +101,13 @@ __device__ __forceinline__ float partner32(float x, bool upper_half)
     return __builtin_bit_cast(float, upper_half ? p[0] : p[1]);
 }
 
+// LDS byte address of a pointer into a __shared__ object (a constant for the
+// object itself).
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane s supplies the
 // address of 4 consecutive 16-bit elements; lane i of the group receives, in
 // slot j, element (i % 4) of the 4 read by lane 4j + i/4.  With lane s pointing

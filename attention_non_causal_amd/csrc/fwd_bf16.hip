@@ -10,20 +10,23 @@
 // (online softmax).
 //
 // Work decomposition
-//   Workgroup = 4 wavefronts = 128 query rows of one (batch, head); each wave
-//   owns 32 rows.  Keys stream through LDS in tiles of 64.  Copies go global ->
-//   LDS by buffer_load_dwordx4 ... lds (no VGPR staging); each lane's buffer
-//   offset within a tile is fixed for the whole kernel and the tile's start is
-//   a scalar offset.  A tile past the last key clamps its rows to the last key,
-//   so every LDS value stays finite.
+//   Each wave owns 32 query rows of one (batch, head).  d = 128: a workgroup
+//   of 8 waves (256 rows), one per CU -- every K/V tile copied into LDS then
+//   serves 256 rows, which halves copy traffic against 4-wave workgroups;
+//   d = 64: 4 waves (128 rows), two workgroups per CU.  Either way each SIMD
+//   runs two waves.  Keys stream through LDS in tiles of 64.  Copies go
+//   global -> LDS by buffer_load_dwordx4 ... lds (no VGPR staging); each
+//   lane's buffer offset within a tile is fixed for the whole kernel and the
+//   tile's start is a scalar offset.  Rows past the last key lie outside the
+//   buffer range and read as zeros, so every LDS value stays finite.
 //   Per tile and wave the matrix work is
 //     S^T (keys x queries) = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from
 //       LDS, B = Q^T held in registers for the whole kernel.  The transpose
 //       puts one query per lane column, so a row maximum or sum is a per-lane
 //       reduction plus one exchange with lane l^32 (v_permlane32_swap).
-//     O^T (channels x queries) += V^T P^T: A = V^T read from the row-major V
-//       tile with ds_read_b64_tr_b16 (LDS transpose read), B = P^T straight from
-//       the S^T accumulator registers.  A and B use the same assignment of keys
+//     O^T (channels x queries) += V^T P^T: A = V^T read from the V tile with
+//       ds_read_b64_tr_b16 (LDS transpose read), B = P^T straight from the S^T
+//       accumulator registers.  A and B use the same assignment of keys
 //       to k slots, so no register shuffle is needed.
 //   Software pipeline: iteration j runs the P V product of tile j-1, the K Q^T
 //   product of tile j+1 and the softmax of tile j.  The three are independent,
@@ -43,11 +46,13 @@
 //   reads K(j+1), V(j-1) from one pair while K(j+2), V(j) are copied into the
 //   other; one barrier per iteration.  (Separate objects also let the compiler
 //   see that the transpose reads never alias an outstanding copy.)
-//   Layout of a tile: rows of D bf16; the 16-byte chunk c of row r sits at
-//   chunk slot c ^ f(r), where f permutes bits of r so that both read patterns
-//   are free of bank conflicts -- 16 rows x one chunk (the K operand) and 4
-//   rows x 4 chunks (the transpose read of V) each cover all 64 banks.  Every
-//   LDS address is a per-lane base (computed once) plus a compile-time offset.
+//   K tile layout: rows of D bf16; the 16-byte chunk c of row r sits at chunk
+//   slot c ^ f(r), where f permutes bits of r so that the K operand read (16
+//   rows x one chunk) covers all 64 banks.  V tile layout: D/32 blocks of 32
+//   channels, each 64 keys x 64 bytes, so a transpose read (4 keys x 64 bytes
+//   per half-wave) covers all 64 banks with no swizzle, and every V read is one
+//   per-lane register plus a constant.  Every LDS address is a per-lane base
+//   (computed once) plus a compile-time offset.
 //   Tails: query rows >= Sq are computed on zero queries and never stored;
 //   keys >= Skv get score -inf.
 #include "common.hpp"
@@ -60,17 +65,20 @@ namespace {
 
 template <int D>
 struct FwdBf16Cfg {
-    static constexpr int kWaves = 4;
+    // d = 128: one workgroup of 8 waves per CU, so 256 query rows share every
+    // K/V tile copied into LDS; d = 64: two workgroups of 4 waves per CU.
+    static constexpr int kWaves = D == 128 ? 8 : 4;
+    static constexpr int kWgPerCu = D == 128 ? 1 : 2;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBr = 32 * kWaves;                // query rows per workgroup
     static constexpr int kBc = 64;                         // keys per tile
     static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
     static constexpr int kRowBytes = D * 2;
     static constexpr int kTileBytes = kBc * kRowBytes;     // one K or V tile
-    static constexpr int kBufBytes = 2 * kTileBytes;       // K tile then V tile
     static constexpr int kLoads = kTileBytes / (16 * kThreads);  // 16-B loads per thread
     static constexpr int kLoadRows = 16 * kThreads / kRowBytes;   // rows one copy covers
     static constexpr int kMB = D / 32;                     // 32-channel output blocks
+    static constexpr int kVBlockBytes = kBc * 64;          // V tile: one 32-channel block
     static constexpr float kRescaleThreshold = 8.0f;       // log2 units
 };
 
@@ -170,10 +178,11 @@ struct FwdBf16Tile {
     uint32_t tok_bytes;
     int key_end, wave, hh;   // keys >= key_end are masked (the end of this block's range)
     float scale_log2;
-    uint32_t ld_voff;        // this lane's offset in copy 0 (copy i: + i * kLoadRows rows)
+    uint32_t k_voff;         // this lane's source offset in K copy 0 (copy i: + i * kLoadRows rows)
+    uint32_t v_voff;         // this lane's source offset in V copy 0 (copy i: + kWaves/4 blocks)
     u32x4 qf[kSteps];        // bf16 operands are carried as raw 32-bit words
     int k_addr[kSteps / 2];  // steps s and s + kSteps/2 differ in one address bit
-    int v_addr[kVReads];
+    uint32_t v_reg;          // LDS address of this lane's V transpose reads in V buffer 0
     f32x16 oacc[kMB];
     f32x16 sacc[2][2];       // [parity][32-key block]: S^T of a tile
     u32x4 pf[2][4];          // [parity][16-key step]: P^T of a tile
@@ -199,11 +208,11 @@ struct FwdBf16Tile {
 #pragma unroll
         for (int i = 0; i < Cfg::kLoads; ++i) {
             const int off = (i * Cfg::kWaves + wave) * 1024;
-            const uint32_t so = soff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes;
             if constexpr (KB >= 0)
-                copy16_to_lds(k_rsrc, kbuf[KB] + off, ld_voff, so);
+                copy16_to_lds(k_rsrc, kbuf[KB] + off, k_voff,
+                              soff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes);
             if constexpr (VB >= 0)
-                copy16_to_lds(v_rsrc, vbuf[VB] + off, ld_voff, so);
+                copy16_to_lds(v_rsrc, vbuf[VB] + off, v_voff, soff + i * (Cfg::kWaves / 4) * 64);
         }
     }
 
@@ -220,11 +229,21 @@ struct FwdBf16Tile {
         kf[Q % 3] = ld_lds16(kbuf[KB] + k_off(Q / 2) + 32 * (Q % 2) * kRow);
     }
 
-    // Transpose read E (block E/2, half E%2) of 16-key step T from V buffer VB.
+    // Transpose read E (block E/2, half E%2) of 16-key step T from V buffer VB:
+    // this lane's address in V buffer 0 plus a constant, written so that the
+    // constant (the buffer's distance from buffer 0, the block, the keys)
+    // folds into the instruction's offset field.
+    template <int VB>
+    __device__ __forceinline__ u32x2 ld_v(int T, int E) const
+    {
+        const int c = (E / 2) * Cfg::kVBlockBytes + (16 * T + 8 * (E % 2)) * 64;
+        return ld_lds_tr16(vbuf[VB] + ((int)v_reg - (int)lds_addr(vbuf[0]) + c));
+    }
+
     template <int VB, int T, int E>
     __device__ __forceinline__ void read_v()
     {
-        vf[E] = ld_lds_tr16(vbuf[VB] + v_addr[E] + 16 * T * kRow);
+        vf[E] = ld_v<VB>(T, E);
     }
 
     // The full S^T of one tile from K buffer KB into sacc[SP] (prologue only).
@@ -418,7 +437,7 @@ struct FwdBf16Tile {
         // operands of the first slots
 #pragma unroll
         for (int e = 0; e < kVReads; ++e)
-            vf[e] = ld_lds_tr16(vbuf[P ^ 1] + v_addr[e]);
+            vf[e] = ld_v<P ^ 1>(0, e);
         read_k<P ^ 1, 0>();
         read_k<P ^ 1, 1>();
         __builtin_amdgcn_sched_barrier(0);
@@ -445,7 +464,7 @@ struct FwdBf16Tile {
 // (ws_o [piece][kBr][D], ws_lse [piece][kBr]); split_merge_kernel combines
 // them with the log-sum-exp merge.
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int H, int Sq, int Skv, float scale_log2, int n_qtiles, int n_main, int nsplit,
@@ -503,14 +522,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         st.v_rsrc = make_rsrc(Vbh, extent);
     }
     // Copy i of wave w fills LDS chunks [(i*kWaves + w)*64, +64) of a tile; lane
-    // l takes chunk p = that base + l, i.e. row p / kChunks at slot p % kChunks,
-    // which holds column chunk (p % kChunks) ^ f(row).
-    // Copy i covers rows i * kLoadRows more than copy 0 and, as f() depends only on
-    // row bits that copy index does not change, the same chunk slots.
+    // l takes chunk p = that base + l.
+    //   K (row-major, swizzled): row p / kChunks at slot p % kChunks, which holds
+    //   column chunk (p % kChunks) ^ f(row).  Copy i covers rows i * kLoadRows
+    //   more than copy 0 and, as f() depends only on row bits that the copy
+    //   index does not change, the same chunk slots.
+    //   V (32-channel blocks of 64 keys x 64 bytes): block p / 256, key
+    //   (p / 4) % 64, 16-byte column chunk p % 4 of the block.  Copy i is
+    //   kWaves/4 blocks further on.
     {
         const int p = st.wave * 64 + lane;
         const int r = p / Cfg::kChunks;
-        st.ld_voff = (uint32_t)r * st.tok_bytes + swz_slot<D>(r, p % Cfg::kChunks) * 16;
+        st.k_voff = (uint32_t)r * st.tok_bytes + swz_slot<D>(r, p % Cfg::kChunks) * 16;
+        st.v_voff = (uint32_t)((p / 4) % 64) * st.tok_bytes + ((p / 256) * 4 + p % 4) * 16;
     }
     // K(kt0), K(kt0+1) for the first two K Q^T products; V(kt0+1) into V buffer
     // 1, where the first iteration's P V (with P = 0) reads finite values.
@@ -538,21 +562,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
     // Per-lane LDS bases.  K operand (A of S^T), step s: row n (+32 for the
     // second block), column 16s + 8hh.  V transpose reads, block mb, half hi:
-    // lane group g = lane/16 reads row 4hh + 8hi + (lane%16)/4 (+16t) at columns
-    // 32mb + 16(g%2) + 4(lane%4) .. +3, so lane l receives channel 32mb + l%32
-    // of keys 16t + 8hi + 4hh + 0..3.
+    // lane group g = lane/16 reads key 4hh + 8hi + (lane%16)/4 (+16t) of block
+    // mb at channels 16(g%2) + 4(lane%4) .. +3, so lane l receives channel
+    // 32mb + l%32 of keys 16t + 8hi + 4hh + 0..3.  (The 32 lanes of one
+    // half-wave cover 4 keys x 64 contiguous bytes: all 64 banks once.)
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
         st.k_addr[s] = lds_byte<D>(n, 16 * s + 8 * hh);
-    {
-        const int vr = 4 * hh + ((lane & 15) >> 2);
-        const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-            for (int hi = 0; hi < 2; ++hi)
-                st.v_addr[2 * mb + hi] = lds_byte<D>(vr + 8 * hi, 32 * mb + vc);
-    }
+    st.v_reg = lds_addr(v_lds0) + (4 * hh + ((lane & 15) >> 2)) * 64 +
+               (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    pin(st.v_reg);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
         st.oacc[mb] = f32x16{};
@@ -667,7 +686,7 @@ FwdSplit plan_d(int B, int H, int Sq, int Skv, int n_cu)
     const long n_qtiles = (Sq + Cfg::kBr - 1) / Cfg::kBr;
     const long n_blocks = n_qtiles * H * B;
     const long n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
-    const long slots = 2L * n_cu;  // two workgroups per CU
+    const long slots = (long)Cfg::kWgPerCu * n_cu;  // workgroups resident at once
     sp.n_main = (int)n_blocks;
     sp.nsplit = 1;
     if (n_cu <= 0 || n_blocks > 0x7fffffffL)

@@ -126,12 +126,13 @@ def test_ws_errors():
 
 
 def test_benchmark_shape_is_split():
-    """The FLUX-like workload leaves a partial last wave (3168 query tiles) on
-    this GPU, so the launch bench.py times splits it."""
+    """The FLUX-like workload (d = 128: 256-row query tiles, one workgroup per
+    CU) leaves a partial last wave (1584 tiles) on this GPU, so the launch
+    bench.py times splits it."""
     W = wl.WORKLOADS["flux"]
     n = _lib.dit_attn_fwd_workspace_size(W.B, W.H, W.Sq, W.Skv, W.d)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     say(f"flux workspace {n} bytes on {n_cu} compute units")
-    tiles = (W.Sq + 127) // 128 * W.H * W.B
-    if tiles % (2 * n_cu) and 2 * (tiles % (2 * n_cu)) <= 2 * n_cu:
+    tiles = (W.Sq + 255) // 256 * W.H * W.B
+    if tiles % n_cu and 2 * (tiles % n_cu) <= n_cu:
         assert n > 0
