@@ -35,13 +35,14 @@
 //   the same slots: the vector ALU works in the shadow of the matrix core
 //   instead of after it.  The slots are fenced (sched_barrier) so the compiler
 //   keeps that order.  LDS operands are read several slots ahead.
-//   Online softmax in the log2 domain: scale*log2(e) is folded into one FMA
-//   before v_exp_f32.  The output is rescaled only when a row maximum grows by
-//   more than 2^8 over the one in use; until then the stale maximum keeps every
-//   weight below 2^8, and the final O / sum and LSE are exact for any maximum,
-//   so this skips almost all rescale multiplies.  The rescale of O is applied
-//   at the end of the iteration, after the P V product of the previous tile
-//   (taken against the old maximum) has been accumulated.
+//   Softmax in the log2 domain: scale*log2(e) is folded into one FMA before
+//   v_exp_f32.  The weights of a whole pass over the keys are taken against one
+//   reference maximum (the first tile's row maximum): the final O / sum and LSE
+//   are exact for any reference as long as no weight overflows, so no tile is
+//   reduced to its maximum and O is never rescaled.  Should a later score rise
+//   so far above the reference that a lane's weight sum for a tile passes
+//   2^32, the workgroup computes the exact row maxima of its key range and
+//   makes the pass again (see the kernel).
 //   LDS: two K and two V tile buffers, each its own LDS object.  Iteration j
 //   reads K(j+1), V(j-1) from one pair while K(j+2), V(j) are copied into the
 //   other; one barrier per iteration.  (Separate objects also let the compiler
@@ -79,7 +80,9 @@ struct FwdBf16Cfg {
     static constexpr int kLoadRows = 16 * kThreads / kRowBytes;   // rows one copy covers
     static constexpr int kMB = D / 32;                     // 32-channel output blocks
     static constexpr int kVBlockBytes = kBc * 64;          // V tile: one 32-channel block
-    static constexpr float kRescaleThreshold = 8.0f;       // log2 units
+    // Bound on one lane's sum of weights of one tile (32 weights), which keeps
+    // every weight <= 2^32: O and the sums cannot overflow for |V| < 2^80.
+    static constexpr float kWeightSumLimit = 0x1p32f;
 };
 
 // Chunk slot of chunk c in row r (see the layout note above).
@@ -170,7 +173,7 @@ struct FwdBf16Tile {
     static constexpr int kSteps = D / 16;          // k steps of K Q^T
     static constexpr int kSlots = D / 4;           // matrix instructions per iteration
     static constexpr int kVReads = 2 * kMB;        // V^T transpose reads per 16-key step
-    static constexpr int kPer = D == 128 ? 3 : 1;  // slots per group of 4 scores
+    static constexpr int kPer = kSlots / 8;        // slots per group of 4 scores
 
     uint8_t* kbuf[2];
     uint8_t* vbuf[2];
@@ -188,14 +191,10 @@ struct FwdBf16Tile {
     u32x4 pf[2][4];          // [parity][16-key step]: P^T of a tile
     u32x2 vf[kVReads];       // V^T fragments of one 16-key step
     u32x4 kf[3];             // K fragments, three in flight
-    float mxc[4];            // partial row maxima
     uint32_t pw[2];          // bf16 pairs of the even group of a 16-key step
     float lsum;              // sum of this lane's weights of the current tile
-    float m_tile;            // row maximum of the current tile (scale*log2(e) units)
-    float alpha;             // rescale factor of this iteration
-    int grow;                // (an int: a bool member makes the optimizer carry its
-                             // neighbours as bytes)
-    float m_used;  // maximum (scale*log2(e) units) the weights are taken against
+    float lsum_max;          // largest lsum of the pass (checked against kWeightSumLimit)
+    float m_used;  // reference maximum (scale*log2(e) units) of the weights, fixed per pass
     float l_run;   // running sum over this lane's half of the keys
 
     // Copy tile kt of K (to K buffer KB) and/or of V (to V buffer VB) into LDS;
@@ -265,109 +264,96 @@ struct FwdBf16Tile {
             vgpr_wait(sacc[SP][kb]);
     }
 
-    // Softmax of the tile in sacc[P], vector work of slot I:
-    //   slots 0-5:  four chains of partial maxima over 8 scores each (32-key
-    //               block kb, registers 8h..8h+7; block 0 in slots 0-3, block 1,
-    //               whose last K Q^T step ends a slot later, in slots 2-5);
-    //   slot 6:     the row maximum (both lane halves);
-    //   slot 7:     the maximum in use and this iteration's rescale factor;
-    //   slots 8..:  8 groups of 4 scores -> weights (in place), sum, bf16 pairs
-    //               (d = 128: weights of two scores per slot, then the sum and
-    //               pairs; d = 64: a group per slot).
-    static constexpr int kGroup0 = 8;
-
-    // Step STEP of the two partial-maximum chains of 32-key block KB.
-    template <int P, int KB, int STEP>
-    __device__ __forceinline__ void max_chains()
-    {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const f32x16& s = sacc[P][KB];
-            const int o = 8 * h;
-            float& m = mxc[2 * KB + h];
-            if constexpr (STEP == 0)
-                m = fmaxf(fmaxf(s[o + 0], s[o + 1]), s[o + 2]);
-            else if constexpr (STEP == 1)
-                m = fmaxf(fmaxf(m, s[o + 3]), s[o + 4]);
-            else if constexpr (STEP == 2)
-                m = fmaxf(fmaxf(m, s[o + 5]), s[o + 6]);
-            else
-                m = fmaxf(m, s[o + 7]);
-            pin(m);
-        }
-    }
-
-    // Re-pin, right after slot I's matrix instruction, the values its vector
-    // work reads, so that work cannot be hoisted into an earlier slot.
-    template <int I>
-    __device__ __forceinline__ void slot_inputs()
-    {
-        if constexpr (I == 6) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                pin(mxc[c]);
-        } else if constexpr (I == 7) {
-            pin(m_tile);
-        } else if constexpr (I >= kGroup0 && I < kGroup0 + 8 * kPer) {
-            pin(m_used);
-        }
-    }
-
+    // Softmax of the tile in sacc[P], vector work of slot I.  The weights are
+    // 2^(scale*log2(e)*s - m_used) with m_used fixed for the whole pass (see
+    // the kernel), so a tile needs no maximum of its own.  8 groups of 4
+    // scores, group G (32-key block G/4) in slots kPer*G .. kPer*G + kPer-1:
+    // the weights (in place) of 4/kPer scores per slot, then in the group's
+    // last slot their sum and bf16 pairs.  Block 1's groups start at slot
+    // 4*kPer >= 2, two matrix instructions after its last K Q^T step.
     template <int P, int I>
     __device__ __forceinline__ void softmax_part()
     {
-        slot_inputs<I>();
-        if constexpr (I < 4)
-            max_chains<P, 0, I>();
-        if constexpr (I >= 2 && I < 6)
-            max_chains<P, 1, I - 2>();
-        if constexpr (I == 6) {
-            const float mx = fmaxf(fmaxf(mxc[0], mxc[1]), fmaxf(mxc[2], mxc[3]));
-            m_tile = fmaxf(mx, partner32(mx, hh)) * scale_log2;
-            pin(m_tile);
-        } else if constexpr (I == 7) {
-            grow = m_tile > m_used + Cfg::kRescaleThreshold;
-            const float m_new = grow ? m_tile : m_used;
-            alpha = exp2_fast(m_used - m_new);
-            m_used = m_new;
-            pin(alpha);
-            pin(m_used);
-            lsum = 0.f;
-        } else if constexpr (I >= kGroup0 && I < kGroup0 + 8 * kPer) {
-            constexpr int G = (I - kGroup0) / kPer;  // group of 4 scores
-            constexpr int sub = (I - kGroup0) % kPer;
-            constexpr int kb = G / 4;
-            constexpr int r0 = 4 * (G % 4);
-            f32x16& s = sacc[P][kb];
-            constexpr int lo = kPer == 1 ? 0 : 2 * sub, hi = kPer == 1 ? 4 : 2 * sub + 2;
-            if constexpr (kPer == 1 || sub < 2) {
+        constexpr int G = I / kPer;  // group of 4 scores
+        constexpr int sub = I % kPer;
+        constexpr int kb = G / 4;
+        constexpr int r0 = 4 * (G % 4);
+        constexpr int kW = 4 / kPer;  // weights per slot
+        // re-pinned each slot, so that this slot's weights cannot be hoisted
+        // into an earlier one
+        pin(m_used);
+        f32x16& s = sacc[P][kb];
 #pragma unroll
-                for (int r = r0 + lo; r < r0 + hi; ++r) {
-                    float e = exp2_fast(__builtin_fmaf(s[r], scale_log2, -m_used));
-                    pin(e);
-                    s[r] = e;
-                }
-            }
-            if constexpr (sub == kPer - 1) {
-                lsum += (s[r0] + s[r0 + 1]) + (s[r0 + 2] + s[r0 + 3]);
-                pin(lsum);
-                // P^T fragment of 16-key step t = registers 8(t%2)..+7 of block
-                // t/2: the even group gives its first two words, the odd group
-                // the last two
-                constexpr int t = 2 * kb + (G % 4) / 2;
-                if constexpr (G % 2 == 0) {
-                    pw[0] = pack_bf16x2(s[r0], s[r0 + 1]);
-                    pw[1] = pack_bf16x2(s[r0 + 2], s[r0 + 3]);
-                    pin(pw[0]);
-                    pin(pw[1]);
-                } else {
-                    u32x4 v = {pw[0], pw[1], pack_bf16x2(s[r0], s[r0 + 1]),
-                               pack_bf16x2(s[r0 + 2], s[r0 + 3])};
-                    pin(v);
-                    pf[P][t] = v;
-                }
+        for (int r = r0 + kW * sub; r < r0 + kW * (sub + 1); ++r) {
+            float e = exp2_fast(__builtin_fmaf(s[r], scale_log2, -m_used));
+            pin(e);
+            s[r] = e;
+        }
+        if constexpr (sub == kPer - 1) {
+            const float g = (s[r0] + s[r0 + 1]) + (s[r0 + 2] + s[r0 + 3]);
+            lsum = G == 0 ? g : lsum + g;
+            pin(lsum);
+            // P^T fragment of 16-key step t = registers 8(t%2)..+7 of block
+            // t/2: the even group gives its first two words, the odd group
+            // the last two
+            constexpr int t = 2 * kb + (G % 4) / 2;
+            if constexpr (G % 2 == 0) {
+                pw[0] = pack_bf16x2(s[r0], s[r0 + 1]);
+                pw[1] = pack_bf16x2(s[r0 + 2], s[r0 + 3]);
+                pin(pw[0]);
+                pin(pw[1]);
+            } else {
+                u32x4 v = {pw[0], pw[1], pack_bf16x2(s[r0], s[r0 + 1]),
+                           pack_bf16x2(s[r0 + 2], s[r0 + 3])};
+                pin(v);
+                pf[P][t] = v;
             }
         }
+    }
+
+    // Scores of keys >= key_end in the tile at key0 (in sacc[SP]) -> -inf.
+    template <int SP>
+    __device__ __forceinline__ void mask_tile(int key0)
+    {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            vgpr_wait(sacc[SP][kb]);  // the last K Q^T steps may still run
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+                if (key >= key_end)
+                    sacc[SP][kb][r] = -INFINITY;
+            }
+    }
+
+    // Row maximum (scale*log2(e) units, both lane halves) of the tile in sacc[SP].
+    template <int SP>
+    __device__ __forceinline__ float tile_max() const
+    {
+        float m = sacc[SP][0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                m = fmaxf(m, sacc[SP][kb][r]);
+        return fmaxf(m, partner32(m, hh)) * scale_log2;
+    }
+
+    // One step of the maximum pass: S^T of the tile kt from K buffer KB (its
+    // copy waited for), the copy of K(kt+1) into the other buffer started.
+    template <int KB>
+    __device__ __forceinline__ void max_step(int kt, float& m)
+    {
+        copy_tile<KB ^ 1, -1>(kt + 1);
+        qk_tile<KB, 0>();
+        const int key0 = kt * kBc;
+        if (key0 + kBc > key_end)
+            mask_tile<0>(key0);
+        m = fmaxf(m, tile_max<0>());
+        wait_vmem_all();
+        __syncthreads();
     }
 
     // Slot I of iteration parity P: one matrix instruction, the LDS reads
@@ -421,19 +407,8 @@ struct FwdBf16Tile {
         copy_tile<-1, P>(kt);
         copy_tile<P, -1>(kt + 2);
         const int key0 = kt * kBc;
-        if (key0 + kBc > key_end) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                vgpr_wait(sacc[P][kb]);  // the last K Q^T steps may still run
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-                    if (key >= key_end)
-                        sacc[P][kb][r] = -INFINITY;
-                }
-        }
+        if (key0 + kBc > key_end)
+            mask_tile<P>(key0);
         // operands of the first slots
 #pragma unroll
         for (int e = 0; e < kVReads; ++e)
@@ -442,15 +417,8 @@ struct FwdBf16Tile {
         read_k<P ^ 1, 1>();
         __builtin_amdgcn_sched_barrier(0);
         slots<P, 0>();
-        l_run = __builtin_fmaf(l_run, alpha, lsum);
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                acc_wait(oacc[mb]);
-                oacc[mb] *= alpha;
-                acc_wait(oacc[mb]);
-            }
-        }
+        l_run += lsum;
+        lsum_max = fmaxf(lsum_max, lsum);
         wait_vmem_all();
         __syncthreads();
     }
@@ -477,6 +445,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[Cfg::kTileBytes];
+    __shared__ int wave_over[Cfg::kWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -536,8 +505,9 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
         st.k_voff = (uint32_t)r * st.tok_bytes + swz_slot<D>(r, p % Cfg::kChunks) * 16;
         st.v_voff = (uint32_t)((p / 4) % 64) * st.tok_bytes + ((p / 256) * 4 + p % 4) * 16;
     }
-    // K(kt0), K(kt0+1) for the first two K Q^T products; V(kt0+1) into V buffer
-    // 1, where the first iteration's P V (with P = 0) reads finite values.
+    // A pass starts with K(kt0), K(kt0+1) for the first two K Q^T products and
+    // V(kt0+1) in V buffer 1, where the first iteration's P V (with P = 0)
+    // reads finite values.  (The first pass's copies overlap the Q loads.)
     st.template copy_tile<0, -1>(kt0);
     st.template copy_tile<1, 1>(kt0 + 1);
 
@@ -572,29 +542,68 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     st.v_reg = lds_addr(v_lds0) + (4 * hh + ((lane & 15) >> 2)) * 64 +
                (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     pin(st.v_reg);
+    // Passes over the key range.  The weights of a pass are taken against one
+    // reference maximum m_used: O / sum and LSE are exact for any reference
+    // as long as no weight overflows, so no tile needs a maximum of its own and
+    // O is never rescaled.  The first pass takes the first tile's row maximum.
+    // If a later score rises so far above it that some lane's weights for a
+    // tile sum past kWeightSumLimit, the workgroup finds the exact row maxima
+    // of the range (a K Q^T-only pass) and makes a second pass against them,
+    // in which no weight exceeds 1.
+    for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-        st.oacc[mb] = f32x16{};
-        acc_wait(st.oacc[mb]);
-    }
+        for (int mb = 0; mb < kMB; ++mb) {
+            st.oacc[mb] = f32x16{};
+            acc_wait(st.oacc[mb]);
+        }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        st.pf[1][t] = u32x4{0, 0, 0, 0};
-    st.m_used = -INFINITY;
-    st.l_run = 0.f;
+        for (int t = 0; t < 4; ++t)
+            st.pf[1][t] = u32x4{0, 0, 0, 0};
+        st.l_run = 0.f;
+        st.lsum_max = 0.f;
 
-    wait_vmem_all();
-    __syncthreads();
-    st.template qk_tile<0, 0>();
-    __syncthreads();  // K buffer 0 is refilled by the first iteration
+        wait_vmem_all();
+        __syncthreads();
+        st.template qk_tile<0, 0>();
+        if (pass == 0) {
+            if (kt0 * Cfg::kBc + Cfg::kBc > st.key_end)
+                st.template mask_tile<0>(kt0 * Cfg::kBc);
+            st.m_used = st.template tile_max<0>();
+        }
+        __syncthreads();  // K buffer 0 is refilled by the first iteration
 
-    // Iterations run in pairs (the buffer index is compile-time); the ones past
-    // the last tile of the range see only masked keys, so their weights are 0,
-    // and the first of them accumulates the last tile's P V.
-    const int n_it = (kt1 - kt0 + 2) & ~1;
-    for (int i = 0; i < n_it; i += 2) {
-        st.template iteration<0>(kt0 + i);
-        st.template iteration<1>(kt0 + i + 1);
+        // Iterations run in pairs (the buffer index is compile-time); the ones
+        // past the last tile of the range see only masked keys, so their
+        // weights are 0, and the first of them accumulates the last tile's P V.
+        const int n_it = (kt1 - kt0 + 2) & ~1;
+        for (int i = 0; i < n_it; i += 2) {
+            st.template iteration<0>(kt0 + i);
+            st.template iteration<1>(kt0 + i + 1);
+        }
+
+        if (lane == 0)
+            wave_over[st.wave] = __builtin_amdgcn_ballot_w64(st.lsum_max > Cfg::kWeightSumLimit) != 0;
+        __syncthreads();
+        int over = 0;
+#pragma unroll
+        for (int w = 0; w < Cfg::kWaves; ++w)
+            over |= wave_over[w];
+        if (!over || pass > 0)
+            break;
+
+        // exact row maxima of the range, then the second pass
+        float m = -INFINITY;
+        st.template copy_tile<0, -1>(kt0);
+        wait_vmem_all();
+        __syncthreads();
+        const int n_mx = (kt1 - kt0 + 1) & ~1;
+        for (int i = 0; i < n_mx; i += 2) {
+            st.template max_step<0>(kt0 + i, m);
+            st.template max_step<1>(kt0 + i + 1, m);
+        }
+        st.m_used = m;
+        st.template copy_tile<0, -1>(kt0);
+        st.template copy_tile<1, 1>(kt0 + 1);
     }
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)

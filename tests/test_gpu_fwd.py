@@ -145,6 +145,67 @@ def test_huge_logits_stay_finite():
             what="Qx100")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("first", [0, 200])
+def test_scores_rising_far_above_the_first_tile(d, first):
+    """Keys from `first + 64` on are scaled up so that later scores exceed the
+    first key tile's row maximum by far more than the weight bound allows: the
+    kernel must find the exact row maxima and redo its pass.  Only head 0 is
+    scaled, so the workgroups of head 1 keep their single pass."""
+    say(f"fwd rising scores d{d} first{first}")
+    B, H, Sq, Skv = 1, 2, 300, 700
+    q, k, v = _draw(B, H, Sq, Skv, d, seed=47 + d + first, norm=True)
+    kf = wl.bf16_bits_to_f32(k).copy()
+    kf[:, first + 64:, 0] *= np.float32(12.0)
+    k12 = wl.f32_to_bf16_bits(kf)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, l = run_fwd(q, k12, v, scale)
+    o_ref, l_ref = oracle.attn_fwd(q, k12, v, scale)
+    # scores of head 0 reach ~50 natural units (~70 log2 units) above the
+    # first tile's maximum
+    compare(o, l, o_ref, l_ref, o_tol=_gpu.few_key_o_tol(v),
+            lse_tol=1e-3 * max(1, np.abs(l_ref).max() / 100), rel_rms=None, what=f"rising d{d}")
+
+
+def test_rising_scores_split_launch():
+    """The same through dit_attn_fwd_ws, whose split pieces each have their
+    own first tile."""
+    say("fwd_ws rising scores")
+    B, H, Sq, Skv, d = 1, 2, 256, 2048, 128
+    n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d)
+    q, k, v = _draw(B, H, Sq, Skv, d, seed=48, norm=True)
+    kf = wl.bf16_bits_to_f32(k).copy()
+    kf[:, 1500:] *= np.float32(12.0)
+    k12 = wl.f32_to_bf16_bits(kf)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    qd, kd, vd = dev_bf16(q), dev_bf16(k12), dev_bf16(v)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=qd.device)
+    o, l = F.attention(qd, kd, vd, scale, workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn_fwd(q, k12, v, scale)
+    compare(host_f64(o), host_f64(l), o_ref, l_ref, o_tol=_gpu.few_key_o_tol(v),
+            lse_tol=1e-3 * max(1, np.abs(l_ref).max() / 100), rel_rms=None, what="rising split")
+
+
+def test_large_values_with_rising_scores():
+    """|V| ~ 2^40 together with scores that rise past the weight bound: the
+    accumulators must not overflow in either pass."""
+    say("fwd large V, rising scores")
+    B, H, Sq, Skv, d = 1, 1, 130, 400, 64
+    q, k, v = _draw(B, H, Sq, Skv, d, seed=49, norm=True)
+    kf = wl.bf16_bits_to_f32(k).copy()
+    kf[:, 100:] *= np.float32(10.0)
+    k10 = wl.f32_to_bf16_bits(kf)
+    vbig = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(v) * np.float32(2.0 ** 40))
+    o, l = run_fwd(q, k10, vbig, 0.125)
+    o_ref, l_ref = oracle.attn_fwd(q, k10, vbig, 0.125)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    err = np.abs(o - o_ref).max()
+    say(f"  max|dO|/2^40 = {err / 2.0 ** 40:.2e}")
+    assert err <= _gpu.few_key_o_tol(vbig)
+    assert np.abs(l - l_ref).max() <= 1e-3 * max(1, np.abs(l_ref).max() / 100)
+
+
 def test_poisoned_tails_and_sentinels():
     """NaN after the last key changes nothing; nothing is written past Sq."""
     say("fwd poisoned tails")
