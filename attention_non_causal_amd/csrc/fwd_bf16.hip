@@ -79,6 +79,11 @@ struct FwdBf16Cfg {
     static constexpr int kLoads = kTileBytes / (16 * kThreads);  // 16-B loads per thread
     static constexpr int kLoadRows = 16 * kThreads / kRowBytes;   // rows one copy covers
     static constexpr int kMB = D / 32;                     // 32-channel output blocks
+    // Slots after whose matrix instruction an iteration issues its V and K
+    // copies (-1: before the first); d = 128 keeps them out of the burst of
+    // LDS reads that follows the barrier.
+    static constexpr int kCopySlotV = D == 128 ? 0 : -1;
+    static constexpr int kCopySlotK = D == 128 ? 8 : -1;
     static constexpr int kVBlockBytes = kBc * 64;          // V tile: one 32-channel block
     // Bound on one lane's sum of weights of one tile (32 weights), which keeps
     // every weight <= 2^32: O and the sums cannot overflow for |V| < 2^80.
@@ -196,6 +201,7 @@ struct FwdBf16Tile {
     float lsum_max;          // largest lsum of the pass (checked against kWeightSumLimit)
     float m_used;  // reference maximum (scale*log2(e) units) of the weights, fixed per pass
     float l_run;   // running sum over this lane's half of the keys
+    int copy_kt;   // tile of the current iteration (for copies issued in its slots)
 
     // Copy tile kt of K (to K buffer KB) and/or of V (to V buffer VB) into LDS;
     // a negative buffer index skips that tensor.  Rows past the last key lie
@@ -387,6 +393,10 @@ struct FwdBf16Tile {
                 read_v<P ^ 1, t, E>();
         }
         softmax_part<P, I>();
+        if constexpr (I == Cfg::kCopySlotV)
+            copy_tile<-1, P>(copy_kt);
+        if constexpr (I == Cfg::kCopySlotK)
+            copy_tile<P, -1>(copy_kt + 2);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -404,8 +414,11 @@ struct FwdBf16Tile {
     template <int P>
     __device__ __forceinline__ void iteration(int kt)
     {
-        copy_tile<-1, P>(kt);
-        copy_tile<P, -1>(kt + 2);
+        copy_kt = kt;
+        if constexpr (Cfg::kCopySlotV < 0)
+            copy_tile<-1, P>(kt);
+        if constexpr (Cfg::kCopySlotK < 0)
+            copy_tile<P, -1>(kt + 2);
         const int key0 = kt * kBc;
         if (key0 + kBc > key_end)
             mask_tile<P>(key0);
