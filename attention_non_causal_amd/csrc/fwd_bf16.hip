@@ -409,6 +409,23 @@ struct FwdBf16Tile {
         }
     }
 
+    // The P V product of the last tile alone (in place of a whole iteration
+    // P, with the same operands: P^T from pf[P^1], V from buffer P^1).
+    template <int P>
+    __device__ __forceinline__ void drain()
+    {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int e = 0; e < kVReads; ++e)
+                vf[e] = ld_v<P ^ 1>(t, e);
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb)
+                mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
+                       pf[P ^ 1][t]);
+        }
+    }
+
     // Iteration kt (parity P = kt % 2): P V of tile kt-1, K Q^T of tile kt+1,
     // softmax of tile kt; copies K(kt+2) and V(kt) into buffers P.
     template <int P>
@@ -585,14 +602,18 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
         }
         __syncthreads();  // K buffer 0 is refilled by the first iteration
 
-        // Iterations run in pairs (the buffer index is compile-time); the ones
-        // past the last tile of the range see only masked keys, so their
-        // weights are 0, and the first of them accumulates the last tile's P V.
-        const int n_it = (kt1 - kt0 + 2) & ~1;
-        for (int i = 0; i < n_it; i += 2) {
+        // One iteration per tile of the range, in pairs (the buffer index is
+        // compile-time), then the last tile's P V: by one more iteration if
+        // the count is odd (its own tile lies past the range: all keys
+        // masked, weights 0), else by drain().
+        const int n_it = kt1 - kt0;
+        int i = 0;
+        for (; i < n_it; i += 2) {
             st.template iteration<0>(kt0 + i);
             st.template iteration<1>(kt0 + i + 1);
         }
+        if (i == n_it)
+            st.template drain<0>();
 
         if (lane == 0)
             wave_over[st.wave] = __builtin_amdgcn_ballot_w64(st.lsum_max > Cfg::kWeightSumLimit) != 0;
