@@ -92,7 +92,8 @@ typedef struct dit_fp8_tensor {
  *       describing an e4m3 tensor and its block scales.  Q.K^T and P.V run on
  *       fp8 MFMA with fp32 accumulation; the block scales are applied inside
  *       the kernel; P is rounded to e4m3 (relative to the running row maximum)
- *       before P.V and the row sum uses the same rounded values.
+ *       before P.V; O is divided by the sum of those rounded weights (so it
+ *       stays a convex combination of values), LSE uses the unrounded ones.
  *   o:   device, bf16 [B][Sq][H][d] (fp32 result rounded to nearest even).
  *   lse: device, fp32 [B][H][Sq].
  *   d:   64 or 128.  Sq, Skv >= 1 (any value: tails are masked).  One batch of K
@@ -108,9 +109,10 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * dit_attn_fwd_workspace_size / dit_attn_fwd_ws -- the bf16 forward pass with
  * caller-provided scratch, used to balance the last wave of workgroups.
  *
- * A launch of dit_attn_fwd runs one workgroup per 128-query tile; when the
- * number of tiles is not a multiple of what the GPU runs at once (two per
- * compute unit), the last wave leaves most of the GPU idle.  dit_attn_fwd_ws
+ * A launch of dit_attn_fwd runs one workgroup per query tile (256 rows for
+ * d = 128, 128 for d = 64); when the number of tiles is not a multiple of
+ * what the GPU runs at once (one per compute unit for d = 128, two for
+ * d = 64), the last wave leaves most of the GPU idle.  dit_attn_fwd_ws
  * runs the leftover tiles split over contiguous ranges of the keys instead
  * (the ring dimension of "xDiT 项目概述" sec. 3.2 applied inside one GPU),
  * writes their partial O and LSE to the workspace and combines them with the
