@@ -196,8 +196,6 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.Skv = Skv;
     a.d = d;
     a.scale = scale;
-    if (dtype != DIT_DTYPE_BF16)
-        return map_hip(dit::launch_fwd_fp8(a, stream));
 
     dit::FwdSplit split = {};
     if (with_ws) {
@@ -205,7 +203,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
         const int st = current_cu_count(&n_cu);
         if (st != DIT_OK)
             return st;
-        split = dit::plan_fwd_bf16_split(B, H, Sq, Skv, d, n_cu);
+        split = dtype == DIT_DTYPE_BF16 ? dit::plan_fwd_bf16_split(B, H, Sq, Skv, d, n_cu)
+                                        : dit::plan_fwd_fp8_split(B, H, Sq, Skv, d, n_cu);
         if (split.n_tail > 0) {
             if (!ws || ws_bytes < split.ws_bytes || !aligned(ws, 16))
                 return DIT_ERR_WORKSPACE;
@@ -215,9 +214,19 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
                     return DIT_ERR_WORKSPACE;
             if (overlap(rw, ro) || overlap(rw, rl))
                 return DIT_ERR_WORKSPACE;
+            if (dtype == DIT_DTYPE_FP8_E4M3) {
+                const int64_t nq = (Sq + DIT_FP8_BLOCK - 1) / DIT_FP8_BLOCK;
+                const int64_t nk = (Skv + DIT_FP8_BLOCK - 1) / DIT_FP8_BLOCK;
+                if (overlap(rw, range(a.q_scale, int64_t(B) * H * nq * 4)) ||
+                    overlap(rw, range(a.k_scale, int64_t(B) * H * nk * 4)) ||
+                    overlap(rw, range(a.v_scale, int64_t(B) * H * nk * 4)))
+                    return DIT_ERR_WORKSPACE;
+            }
             a.ws = ws;
         }
     }
+    if (dtype != DIT_DTYPE_BF16)
+        return map_hip(dit::launch_fwd_fp8(a, split, stream));
     return map_hip(dit::launch_fwd_bf16(a, split, stream));
 }
 
@@ -239,13 +248,12 @@ int dit_attn_fwd_workspace_size(int B, int H, int Sq, int Skv, int d, int dtype,
     if (st != DIT_OK)
         return st;
     *bytes = 0;
-    if (dtype != DIT_DTYPE_BF16)
-        return DIT_OK;
     int n_cu = 0;
     const int hs = current_cu_count(&n_cu);
     if (hs != DIT_OK)
         return hs;
-    *bytes = dit::plan_fwd_bf16_split(B, H, Sq, Skv, d, n_cu).ws_bytes;
+    *bytes = dtype == DIT_DTYPE_BF16 ? dit::plan_fwd_bf16_split(B, H, Sq, Skv, d, n_cu).ws_bytes
+                                     : dit::plan_fwd_fp8_split(B, H, Sq, Skv, d, n_cu).ws_bytes;
     return DIT_OK;
 }
 

@@ -59,7 +59,6 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-#include <algorithm>
 
 namespace dit {
 namespace {
@@ -459,8 +458,8 @@ struct FwdBf16Tile {
 // would end with) are each split into nsplit pieces over contiguous ranges of
 // key tiles, so they fill the machine instead of leaving most of it idle.  A
 // piece writes its normalised fp32 partial O and its LSE to the workspace
-// (ws_o [piece][kBr][D], ws_lse [piece][kBr]); split_merge_kernel combines
-// them with the log-sum-exp merge.
+// (ws_o [piece][kBr][D], ws_lse [piece][kBr]); launch_split_merge (split.hip)
+// combines them with the log-sum-exp merge.
 template <int D>
 __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -675,77 +674,13 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     }
 }
 
-// Combine the nsplit partial results of each split query tile:
-//     M = max_p LSE_p,  w_p = exp(LSE_p - M),
-//     O = sum_p w_p O_p / sum_p w_p,  LSE = M + ln sum_p w_p.
-// One thread per (split tile, row, 4 channels).
-template <int D>
-__global__ __launch_bounds__(256) void split_merge_kernel(
-    const float* __restrict__ ws_o, const float* __restrict__ ws_lse, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, int H, int Sq, int n_qtiles, int n_main, int nsplit, int n_tail)
-{
-    constexpr int kBr = FwdBf16Cfg<D>::kBr;
-    constexpr int kChunks = D / 4;
-    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long)n_tail * kBr * kChunks)
-        return;
-    const int c = (int)(idx % kChunks);
-    const int r = (int)((idx / kChunks) % kBr);
-    const int t = (int)(idx / ((long)kChunks * kBr));
-    const int tile = n_main + t;
-    const int qt = tile % n_qtiles;
-    const int bh = tile / n_qtiles;
-    const int h = bh % H;
-    const int b = bh / H;
-    const int q_row = qt * kBr + r;
-    if (q_row >= Sq)
-        return;
-    const long p0 = (long)t * nsplit;
-    float m = -INFINITY;
-    for (int p = 0; p < nsplit; ++p)
-        m = fmaxf(m, ws_lse[(p0 + p) * kBr + r]);
-    float wsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < nsplit; ++p) {
-        const float w = exp2_fast((ws_lse[(p0 + p) * kBr + r] - m) * kLog2e);
-        const f32x4 o = *reinterpret_cast<const f32x4*>(ws_o + ((p0 + p) * kBr + r) * D + 4 * c);
-        acc += w * o;
-        wsum += w;
-    }
-    const float inv = 1.f / wsum;
-    u32x2 out;
-    out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(O + (((long)b * Sq + q_row) * H + h) * D + 4 * c) = out;
-    if (c == 0)
-        LSE[((long)b * H + h) * Sq + q_row] = m + log2_fast(wsum) * kLn2;
-}
-
 template <int D>
 FwdSplit plan_d(int B, int H, int Sq, int Skv, int n_cu)
 {
     using Cfg = FwdBf16Cfg<D>;
-    FwdSplit sp = {};
-    const long n_qtiles = (Sq + Cfg::kBr - 1) / Cfg::kBr;
-    const long n_blocks = n_qtiles * H * B;
+    const long n_blocks = (long)((Sq + Cfg::kBr - 1) / Cfg::kBr) * H * B;
     const long n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
-    const long slots = (long)Cfg::kWgPerCu * n_cu;  // workgroups resident at once
-    sp.n_main = (int)n_blocks;
-    sp.nsplit = 1;
-    if (n_cu <= 0 || n_blocks > 0x7fffffffL)
-        return sp;
-    const long rem = n_blocks % slots;
-    // split only a last wave that would leave at least half of the machine idle,
-    // into pieces of at least 4 key tiles
-    long nsplit = rem > 0 ? slots / rem : 0;
-    nsplit = std::min({nsplit, n_kt / 4, (long)kMaxSplit});
-    if (rem == 0 || 2 * rem > slots || nsplit < 2)
-        return sp;
-    sp.n_main = (int)(n_blocks - rem);
-    sp.nsplit = (int)nsplit;
-    sp.n_tail = (int)rem;
-    sp.ws_bytes = (size_t)(rem * nsplit) * Cfg::kBr * (D + 1) * sizeof(float);
-    return sp;
+    return plan_split(n_blocks, n_kt, Cfg::kBr, Cfg::kWgPerCu, n_cu, D + 1);
 }
 
 template <int D>
@@ -767,11 +702,7 @@ hipError_t launch_fwd_bf16_d(const FwdArgs& a, const FwdSplit& sp, hipStream_t s
                                  split ? sp.nsplit : 1, ws_o, ws_lse);
     if (e != hipSuccess || !split)
         return e;
-    const long n_threads = (long)sp.n_tail * Cfg::kBr * (D / 4);
-    return launch_kernel(split_merge_kernel<D>, dim3((unsigned)((n_threads + 255) / 256)),
-                         dim3(256), stream, (const float*)ws_o, (const float*)ws_lse,
-                         static_cast<uint16_t*>(a.o), a.lse, a.H, a.Sq, n_qtiles, sp.n_main,
-                         sp.nsplit, sp.n_tail);
+    return launch_split_merge(a, sp, Cfg::kBr, n_qtiles, ws_o, ws_lse, nullptr, stream);
 }
 
 }  // namespace

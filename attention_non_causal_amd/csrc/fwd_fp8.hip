@@ -123,7 +123,7 @@ struct FwdFp8Tile {
     uint8_t* smem;
     __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
     uint32_t tok_bytes;
-    int Skv, n_kt, wave, hh;
+    int Skv, kt_end, wave, hh;  // key tiles up to kt_end (exclusive) are processed
     float qc;                // q_scale * scale * log2(e) of this query tile
     const float* ks;         // k scales of this (b, h)
     const float* vs;         // v scales of this (b, h)
@@ -168,7 +168,7 @@ struct FwdFp8Tile {
         constexpr int KOFF = BUF * Cfg::kBufBytes;
         constexpr int VOFF = KOFF + kTile;
         const int key0 = kt * kBc;
-        if (kt + 1 < n_kt)
+        if (kt + 1 < kt_end)
             issue<BUF ^ 1>(kt + 1);
         const uint8_t* sm = smem;
 
@@ -289,12 +289,20 @@ struct FwdFp8Tile {
     }
 };
 
+// Grid: blocks [0, n_main) each take one query tile over all keys; with a
+// split launch the remaining tiles are each split into nsplit pieces over
+// contiguous ranges of key tiles, which write normalised fp32 O, LSE and the
+// log of their rounded-weight sum (the sum O was normalised by) to the
+// workspace: ws_o [piece][kBr][D], ws_lse [piece][kBr], ws_lr [piece][kBr].
+// The merge weights each piece's O by its rounded-weight sum, so the merged O
+// is again sum_j P~_j v_j / sum_j P~_j over all keys.
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int Sq, int Skv, float scale_log2,
-    int n_qtiles, int n_blocks)
+    int n_qtiles, int n_main, int nsplit, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    float* __restrict__ ws_lr)
 {
     using Cfg = FwdFp8Cfg<D>;
     constexpr int kMB = Cfg::kMB;
@@ -305,7 +313,20 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     const int n = lane & 31;
     const int hh = lane >> 5;
 
-    const int logical = xcd_remap(blockIdx.x, n_blocks);
+    const int n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
+    int logical, kt0, kt1, piece;
+    if ((int)blockIdx.x < n_main) {
+        logical = xcd_remap(blockIdx.x, n_main);
+        kt0 = 0;
+        kt1 = n_kt;
+        piece = -1;
+    } else {
+        piece = blockIdx.x - n_main;
+        logical = n_main + piece / nsplit;
+        const int part = piece % nsplit;
+        kt0 = (int)((long)part * n_kt / nsplit);
+        kt1 = (int)((long)(part + 1) * n_kt / nsplit);
+    }
     const int qt = logical % n_qtiles;
     const int bh = logical / n_qtiles;
     const int h = bh % H;
@@ -319,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     st.hh = hh;
     st.Skv = Skv;
-    st.n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
+    st.kt_end = kt1;
     st.tok_bytes = (uint32_t)tok;
     // the query tile of 128 rows is exactly query block qt
     st.qc = QS[(long)bh * nqb + qt] * scale_log2;
@@ -339,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         st.ld_row[i] = r;
         st.ld_voff[i] = (uint32_t)r * st.tok_bytes + fp8_slot<D>(r, p % Cfg::kChunks) * 16;
     }
-    st.template issue<0>(0);
+    st.template issue<0>(kt0);
 
     const int q_row = qt * Cfg::kBr + st.wave * 32 + n;
     if (q_row < Sq) {
@@ -383,15 +404,31 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     wait_vmem_all();
     __syncthreads();
 
-    for (int kt = 0; kt < st.n_kt; kt += 2) {
+    for (int kt = kt0; kt < kt1; kt += 2) {
         st.template step<0>(kt);
-        if (kt + 1 < st.n_kt)
+        if (kt + 1 < kt1)
             st.template step<1>(kt + 1);
     }
 
     const float l_tot = st.l_run + partner32(st.l_run, hh);
     const float inv = 1.f / (st.lr_run * Cfg::kPScale);
-    if (q_row < Sq) {
+    if (piece >= 0) {
+        // partial result of a split tile
+        const int r = st.wave * 32 + n;
+        float* dst = ws_o + ((long)piece * Cfg::kBr + r) * D + 4 * hh;
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 w = {st.oacc[mb][4 * g + 0] * inv, st.oacc[mb][4 * g + 1] * inv,
+                           st.oacc[mb][4 * g + 2] * inv, st.oacc[mb][4 * g + 3] * inv};
+                *reinterpret_cast<f32x4*>(dst + 32 * mb + 8 * g) = w;
+            }
+        if (hh == 0) {
+            ws_lse[(long)piece * Cfg::kBr + r] = (st.m_used + log2_fast(l_tot)) * kLn2;
+            ws_lr[(long)piece * Cfg::kBr + r] = (st.m_used + log2_fast(st.lr_run)) * kLn2;
+        }
+    } else if (q_row < Sq) {
         uint16_t* dst = O + ((long)b * Sq * H + h) * D + (long)q_row * tok + 4 * hh;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
@@ -408,7 +445,16 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
 }
 
 template <int D>
-hipError_t launch_fwd_fp8_d(const FwdArgs& a, hipStream_t stream)
+FwdSplit plan_d(int B, int H, int Sq, int Skv, int n_cu)
+{
+    using Cfg = FwdFp8Cfg<D>;
+    const long n_blocks = (long)((Sq + Cfg::kBr - 1) / Cfg::kBr) * H * B;
+    const long n_kt = (Skv + Cfg::kBc - 1) / Cfg::kBc;
+    return plan_split(n_blocks, n_kt, Cfg::kBr, 2, n_cu, D + 2);
+}
+
+template <int D>
+hipError_t launch_fwd_fp8_d(const FwdArgs& a, const FwdSplit& sp, hipStream_t stream)
 {
     using Cfg = FwdFp8Cfg<D>;
     const int n_qtiles = (a.Sq + Cfg::kBr - 1) / Cfg::kBr;
@@ -416,16 +462,33 @@ hipError_t launch_fwd_fp8_d(const FwdArgs& a, hipStream_t stream)
     if (n_blocks > 0x7fffffffL)
         return hipErrorInvalidConfiguration;
     const float scale_log2 = a.scale * kLog2e;
-    return launch_kernel(fwd_fp8_kernel<D>, dim3((unsigned)n_blocks), dim3(Cfg::kThreads),
-                         stream, a.q, a.k, a.v, a.q_scale, a.k_scale, a.v_scale, a.o, a.lse, a.H,
-                         a.Sq, a.Skv, scale_log2, n_qtiles, (int)n_blocks);
+    const bool split = sp.n_tail > 0;
+    const size_t n_rows = split ? (size_t)sp.n_tail * sp.nsplit * Cfg::kBr : 0;
+    float* ws_o = split ? static_cast<float*>(a.ws) : nullptr;
+    float* ws_lse = split ? ws_o + n_rows * D : nullptr;
+    float* ws_lr = split ? ws_lse + n_rows : nullptr;
+    const long grid = split ? (long)sp.n_main + (long)sp.n_tail * sp.nsplit : n_blocks;
+    hipError_t e = launch_kernel(fwd_fp8_kernel<D>, dim3((unsigned)grid), dim3(Cfg::kThreads),
+                                 stream, a.q, a.k, a.v, a.q_scale, a.k_scale, a.v_scale, a.o,
+                                 a.lse, a.H, a.Sq, a.Skv, scale_log2, n_qtiles,
+                                 split ? sp.n_main : (int)n_blocks, split ? sp.nsplit : 1, ws_o,
+                                 ws_lse, ws_lr);
+    if (e != hipSuccess || !split)
+        return e;
+    return launch_split_merge(a, sp, Cfg::kBr, n_qtiles, ws_o, ws_lse, ws_lr, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream)
+FwdSplit plan_fwd_fp8_split(int B, int H, int Sq, int Skv, int d, int n_cu)
 {
-    return a.d == 64 ? launch_fwd_fp8_d<64>(a, stream) : launch_fwd_fp8_d<128>(a, stream);
+    return d == 64 ? plan_d<64>(B, H, Sq, Skv, n_cu) : plan_d<128>(B, H, Sq, Skv, n_cu);
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, const FwdSplit& split, hipStream_t stream)
+{
+    return a.d == 64 ? launch_fwd_fp8_d<64>(a, split, stream)
+                     : launch_fwd_fp8_d<128>(a, split, stream);
 }
 
 }  // namespace dit

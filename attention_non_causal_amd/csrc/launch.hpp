@@ -17,13 +17,13 @@ struct FwdArgs {
     float* lse;            // fp32 [B][H][Sq]
     int B, H, Sq, Skv, d;
     float scale;
-    void* ws;              // bf16 path: workspace of the split launch (see FwdSplit)
+    void* ws;              // workspace of the split launch (see FwdSplit)
 };
 
-// Split plan of the bf16 forward pass (fwd_bf16.hip): the first n_main query
-// tiles run over all keys, the last n_tail are split into nsplit pieces over
-// the keys, whose partial results need ws_bytes of workspace (n_tail == 0: no
-// split, no workspace).
+// Split plan of a forward launch (split.hip): the first n_main query tiles run
+// over all keys, the last n_tail are split into nsplit pieces over the keys,
+// whose partial results need ws_bytes of workspace (n_tail == 0: no split, no
+// workspace).
 constexpr int kMaxSplit = 16;
 
 struct FwdSplit {
@@ -42,9 +42,22 @@ struct MergeArgs {
     int B, H, Sq, d;
 };
 
+// n_blocks query tiles of `rows` rows over n_kt key tiles, wg_per_cu
+// workgroups resident per CU; a piece's partial result takes floats_per_row
+// fp32 values per row.
+FwdSplit plan_split(long n_blocks, long n_kt, int rows, int wg_per_cu, int n_cu,
+                    int floats_per_row);
+// Merge the pieces: ws_o [piece][rows][d] normalised O, ws_lse [piece][rows]
+// natural-log LSE, ws_w [piece][rows] the log of the sum each O was
+// normalised by (nullptr: the same as ws_lse).
+hipError_t launch_split_merge(const FwdArgs& a, const FwdSplit& sp, int rows, int n_qtiles,
+                              const float* ws_o, const float* ws_lse, const float* ws_w,
+                              hipStream_t stream);
+
 FwdSplit plan_fwd_bf16_split(int B, int H, int Sq, int Skv, int d, int n_cu);
 hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdSplit& split, hipStream_t stream);
-hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+FwdSplit plan_fwd_fp8_split(int B, int H, int Sq, int Skv, int d, int n_cu);
+hipError_t launch_fwd_fp8(const FwdArgs& a, const FwdSplit& split, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8(const void* x, void* x8, float* scale, int B, int H, int S, int d,
                             hipStream_t stream);

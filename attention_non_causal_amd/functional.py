@@ -76,8 +76,11 @@ def quantize_fp8(x, stream=None):
 
 
 def attention_fp8(q8, q_scale, k8, k_scale, v8, v_scale, scale: float | None = None,
-                  out=None, lse=None, stream=None):
-    """fp8 (e4m3) non-causal attention on quantised inputs from quantize_fp8."""
+                  out=None, lse=None, stream=None, workspace="auto"):
+    """fp8 (e4m3) non-causal attention on quantised inputs from quantize_fp8.
+
+    workspace: as for attention ("auto": dit_attn_fwd_ws with allocated
+    scratch; a uint8 device tensor: that scratch; None: dit_attn_fwd)."""
     import torch
     B, Sq, H, d = q8.shape
     Skv = k8.shape[1]
@@ -90,8 +93,17 @@ def attention_fp8(q8, q_scale, k8, k_scale, v8, v_scale, scale: float | None = N
     dq = _lib.fp8_tensor(q8, q_scale)
     dk = _lib.fp8_tensor(k8, k_scale)
     dv = _lib.fp8_tensor(v8, v_scale)
-    _lib.dit_attn_fwd(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_FP8_E4M3,
-                      stream)
+    if workspace is None:
+        _lib.dit_attn_fwd(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale,
+                          _lib.DIT_DTYPE_FP8_E4M3, stream)
+        return out, lse
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        workspace = workspace_for(q8, k8, _lib.DIT_DTYPE_FP8_E4M3)
+    n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.dit_attn_fwd_ws(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale,
+                         _lib.DIT_DTYPE_FP8_E4M3, workspace, n_bytes, stream)
     return out, lse
 
 

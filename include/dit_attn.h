@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DIT_ATTN_VERSION 10100 /* major*10000 + minor*100 + patch */
+#define DIT_ATTN_VERSION 10200 /* major*10000 + minor*100 + patch */
 
 enum dit_status {
     DIT_OK = 0,
@@ -106,18 +106,20 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
- * dit_attn_fwd_workspace_size / dit_attn_fwd_ws -- the bf16 forward pass with
+ * dit_attn_fwd_workspace_size / dit_attn_fwd_ws -- the forward pass with
  * caller-provided scratch, used to balance the last wave of workgroups.
  *
- * A launch of dit_attn_fwd runs one workgroup per query tile (256 rows for
- * d = 128, 128 for d = 64); when the number of tiles is not a multiple of
- * what the GPU runs at once (one per compute unit for d = 128, two for
- * d = 64), the last wave leaves most of the GPU idle.  dit_attn_fwd_ws
+ * A launch of dit_attn_fwd runs one workgroup per query tile (bf16: 256 rows
+ * for d = 128, one per compute unit at a time, 128 rows for d = 64, two per
+ * compute unit; fp8: 128 rows, two per compute unit); when the number of
+ * tiles is not a multiple of what the GPU runs at once, the last wave leaves
+ * most of the GPU idle.  dit_attn_fwd_ws
  * runs the leftover tiles split over contiguous ranges of the keys instead
  * (the ring dimension of "xDiT 项目概述" sec. 3.2 applied inside one GPU),
  * writes their partial O and LSE to the workspace and combines them with the
  * log-sum-exp merge (as dit_attn_merge does).  Results equal dit_attn_fwd's
- * up to fp32 rounding order.
+ * up to fp32 rounding order (fp8: and the e4m3 rounding of the weights, which
+ * a piece takes against its own running maximum).
  *
  * dit_attn_fwd_workspace_size: *bytes = the workspace the call needs for this
  *   shape on the current HIP device (0 if nothing is split: then workspace may
@@ -127,8 +129,7 @@ int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *   workspace: device memory of workspace_bytes bytes, 16-byte aligned, owned
  *   by the caller, not overlapping any tensor; its contents on entry do not
  *   matter and on return are unspecified.  Calls that may run concurrently
- *   need separate workspaces.  With dtype DIT_DTYPE_FP8_E4M3 the workspace is
- *   not used (size 0) and the call equals dit_attn_fwd.
+ *   need separate workspaces.
  *   Errors as dit_attn_fwd, plus DIT_ERR_WORKSPACE.  The required size is
  *   checked against the current device after the other arguments.
  */

@@ -31,12 +31,15 @@ from tests._gpu import FP8_O_TOL, compare, dev_bf16, host_f64, say
 pytestmark = pytest.mark.gpu
 
 
-def run_fp8(g, scale):
+def run_fp8(g, scale, workspace="auto"):
+    """The fp8 path as the library's users call it: dit_attn_fwd_ws (which
+    splits the last wave of query tiles when the shape leaves one) by default,
+    dit_attn_fwd with workspace=None."""
     q, k, v = dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"])
     q8, qs = F.quantize_fp8(q)
     k8, ks = F.quantize_fp8(k)
     v8, vs = F.quantize_fp8(v)
-    o, l = F.attention_fp8(q8, qs, k8, ks, v8, vs, scale)
+    o, l = F.attention_fp8(q8, qs, k8, ks, v8, vs, scale, workspace=workspace)
     torch.cuda.synchronize()
     return host_f64(o), host_f64(l)
 
@@ -66,8 +69,8 @@ def kernel_bound(qd, kd, vd, scale, rows=None):
     return out
 
 
-def check_against_dequant(g, scale, rows=None, what=""):
-    o, l = run_fp8(g, scale)
+def check_against_dequant(g, scale, rows=None, what="", workspace="auto"):
+    o, l = run_fp8(g, scale, workspace)
     qd, kd, vd = dequant(g["q"]), dequant(g["k"]), dequant(g["v"])
     o_ref, l_ref = oracle.attn_fwd(qd, kd, vd, scale, rows=rows)
     if rows is not None:
@@ -112,6 +115,38 @@ def test_fp8_block_scales_vary_along_keys():
             x[:, 128 * blk:128 * (blk + 1)] *= np.float32(f)
         g[name] = wl.f32_to_bf16_bits(x)
     check_against_dequant(g, float(np.float32(1 / math.sqrt(d))), what="fp8 varying scales")
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,d", [(1, 2, 256, 2048, 128), (2, 3, 300, 1000, 64),
+                                          (1, 1, 1, 5000, 128)])
+def test_fp8_split_launch(B, H, Sq, Skv, d):
+    """Shapes whose last wave of query tiles is split over the keys: the merged
+    O is sum_j P~_j v_j / sum_j P~_j over all keys (each piece's O is weighted
+    by its rounded-weight sum), so the per-element bound holds as for the
+    unsplit launch; the two launches agree to twice that bound."""
+    from attention_non_causal_amd import _lib
+    say(f"fp8 split B{B} H{H} Sq{Sq} Skv{Skv} d{d}")
+    assert _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d, _lib.DIT_DTYPE_FP8_E4M3) > 0, \
+        "this shape is expected to be split"
+    g = wl.generate("flux", seed=950 + Sq + Skv + d, B=B, H=H, Sq=Sq, Skv=Skv, d=d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, l = check_against_dequant(g, scale, what=f"fp8 split B{B}H{H}Sq{Sq}Skv{Skv}d{d}")
+    o1, l1 = run_fp8(g, scale, workspace=None)
+    qd, kd, vd = dequant(g["q"]), dequant(g["k"]), dequant(g["v"])
+    bound = kernel_bound(qd, kd, vd, scale)
+    say(f"  split vs unsplit: max|dO| {np.abs(o - o1).max():.2e} max|dLSE| {np.abs(l - l1).max():.2e}")
+    assert (np.abs(o - o1) <= 2 * bound).all()
+    assert np.abs(l - l1).max() <= 2e-3
+
+
+def test_fp8_split_deterministic():
+    say("fp8 split determinism")
+    g = wl.generate("flux", seed=903, B=1, H=2, Sq=256, Skv=2048, d=128)
+    o1, l1 = run_fp8(g, 0.088)
+    for _ in range(3):
+        o2, l2 = run_fp8(g, 0.088)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
 
 
 def test_fp8_deterministic():
