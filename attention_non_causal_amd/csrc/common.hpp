@@ -121,6 +121,19 @@ __device__ __forceinline__ u32x2 ld_lds_tr16(const void* p)
     return __builtin_bit_cast(u32x2, v);
 }
 
+// ds_read_b64_tr_b8: the byte analogue -- within each group of 16 lanes, lane
+// s supplies the address of 8 consecutive bytes; lane i receives, in byte j,
+// byte (i % 8) of the 8 read by lane 2j + i/8.  With lane s pointing at row
+// s/2, bytes 8(s%2)..+7 of a row-major tile, lane i gets column i of rows
+// 0..7: an 8 x 16 block arrives transposed.
+__device__ __forceinline__ u32x2 ld_lds_tr8(const void* p)
+{
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 // Buffer resource over [base, base + bytes) for raw (unstrided) buffer loads;
 // an access past `bytes` reads zeros instead of faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes)

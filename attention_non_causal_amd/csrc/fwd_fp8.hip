@@ -50,7 +50,6 @@ struct FwdFp8Cfg {
     static constexpr int kRowBytes = D;                   // one e4m3 row
     static constexpr int kChunks = D / 16;                // 16-byte chunks per row
     static constexpr int kTileBytes = kBc * kRowBytes;
-    static constexpr int kBufBytes = 2 * kTileBytes;      // K tile then V tile
     static constexpr int kLoads = kTileBytes / (16 * kThreads);
     static constexpr int kMB = D / 32;                    // 32-channel output blocks
     static constexpr int kKSteps = D / 64;                // MFMA k-steps of Q.K^T
@@ -84,25 +83,15 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c, 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
 
-// Four transpose reads (8 bytes each) at a + OFF + t * ROW16, t = 0..3,
-// completed before return.
-template <int OFF, int ROW16>
-__device__ __forceinline__ i32x8 tr8_read4(int a)
+// Four transpose reads (8 bytes each) at p + t * ROW16, t = 0..3: the V^T
+// operand of one 32x32x64 MFMA (keys 16t..16t+15 in dwords 2t, 2t+1).
+template <int ROW16>
+__device__ __forceinline__ i32x8 tr8_read4(const uint8_t* p)
 {
-    u32x2 o0, o1, o2, o3;
-    asm volatile(
-        "ds_read_b64_tr_b8 %0, %4 offset:%5\n\t"
-        "ds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
-        "ds_read_b64_tr_b8 %2, %4 offset:%7\n\t"
-        "ds_read_b64_tr_b8 %3, %4 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3)
-        : "v"(a), "i"(OFF), "i"(OFF + ROW16), "i"(OFF + 2 * ROW16), "i"(OFF + 3 * ROW16)
-        : "memory");
-    i32x8 r;
-    r[0] = (int)o0[0]; r[1] = (int)o0[1]; r[2] = (int)o1[0]; r[3] = (int)o1[1];
-    r[4] = (int)o2[0]; r[5] = (int)o2[1]; r[6] = (int)o3[0]; r[7] = (int)o3[1];
-    return r;
+    const u32x2 o0 = ld_lds_tr8(p), o1 = ld_lds_tr8(p + ROW16), o2 = ld_lds_tr8(p + 2 * ROW16),
+                o3 = ld_lds_tr8(p + 3 * ROW16);
+    return i32x8{(int)o0[0], (int)o0[1], (int)o1[0], (int)o1[1],
+                 (int)o2[0], (int)o2[1], (int)o3[0], (int)o3[1]};
 }
 
 // Pack 4 fp32 into 4 e4m3 bytes (round to nearest even; inputs <= 448).
@@ -117,10 +106,10 @@ template <int D>
 struct FwdFp8Tile {
     using Cfg = FwdFp8Cfg<D>;
     static constexpr int kBc = Cfg::kBc;
-    static constexpr int kTile = Cfg::kTileBytes;
     static constexpr int kMB = Cfg::kMB;
 
-    uint8_t* smem;
+    uint8_t* kbuf[2];        // K and V tile buffers, each its own LDS object, so the
+    uint8_t* vbuf[2];        // compiler sees operand reads never alias a copy in flight
     __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
     uint32_t tok_bytes;
     int Skv, kt_end, wave, hh;  // key tiles up to kt_end (exclusive) are processed
@@ -142,22 +131,21 @@ struct FwdFp8Tile {
     {
         const int key0 = kt_next * kBc;
         const uint32_t soff = (uint32_t)key0 * tok_bytes;
-        uint8_t* base = smem + BUF * Cfg::kBufBytes;
         if (key0 + kBc <= Skv) {
 #pragma unroll
             for (int i = 0; i < Cfg::kLoads; ++i) {
-                uint8_t* dst = base + (i * Cfg::kWaves + wave) * 1024;
-                copy16_to_lds(k_rsrc, dst, ld_voff[i], soff);
-                copy16_to_lds(v_rsrc, dst + kTile, ld_voff[i], soff);
+                const int off = (i * Cfg::kWaves + wave) * 1024;
+                copy16_to_lds(k_rsrc, kbuf[BUF] + off, ld_voff[i], soff);
+                copy16_to_lds(v_rsrc, vbuf[BUF] + off, ld_voff[i], soff);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < Cfg::kLoads; ++i) {
-                uint8_t* dst = base + (i * Cfg::kWaves + wave) * 1024;
+                const int off = (i * Cfg::kWaves + wave) * 1024;
                 const int over = max(key0 + ld_row[i] - (Skv - 1), 0);
                 const uint32_t vo = ld_voff[i] - (uint32_t)over * tok_bytes;
-                copy16_to_lds(k_rsrc, dst, vo, soff);
-                copy16_to_lds(v_rsrc, dst + kTile, vo, soff);
+                copy16_to_lds(k_rsrc, kbuf[BUF] + off, vo, soff);
+                copy16_to_lds(v_rsrc, vbuf[BUF] + off, vo, soff);
             }
         }
     }
@@ -165,12 +153,9 @@ struct FwdFp8Tile {
     template <int BUF>
     __device__ __forceinline__ void step(int kt)
     {
-        constexpr int KOFF = BUF * Cfg::kBufBytes;
-        constexpr int VOFF = KOFF + kTile;
         const int key0 = kt * kBc;
         if (kt + 1 < kt_end)
             issue<BUF ^ 1>(kt + 1);
-        const uint8_t* sm = smem;
 
         // block scales of this key tile (uniform): both lie in block key0/128
         const int kblk = key0 / Cfg::kScaleBlock;
@@ -186,8 +171,8 @@ struct FwdFp8Tile {
         for (int s = 0; s < Cfg::kKSteps; ++s)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 lo = ld_lds16(sm + k_addr[s][0] + KOFF + 32 * kb * D);
-                const u32x4 hi = ld_lds16(sm + k_addr[s][1] + KOFF + 32 * kb * D);
+                const u32x4 lo = ld_lds16(kbuf[BUF] + k_addr[s][0] + 32 * kb * D);
+                const u32x4 hi = ld_lds16(kbuf[BUF] + k_addr[s][1] + 32 * kb * D);
                 i32x8 a;
                 a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
                 a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
@@ -261,28 +246,18 @@ struct FwdFp8Tile {
         // O^T += V8^T P''^T, P'' carrying the 2^e part of the V block scale
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-            const i32x8 va = tr8_read4<VOFF, 16 * D>(v_addr[mb]);
+            const i32x8 va = tr8_read4<16 * D>(vbuf[BUF] + v_addr[mb]);
             oacc[mb] = mfma_fp8_32x32x64(va, pf, oacc[mb], vexp);
         }
 
         // Sum of the rounded weights of this tile: every row of ones^T P''^T
-        // holds it (the same value in both lane halves).  It is taken after the
-        // transpose reads and consumed at once (all of its result registers are
-        // read, which waits for the whole MFMA): the transpose reads are written
-        // out in asm, and registers freed by a partly consumed MFMA result that
-        // is still in flight must never be handed to them.
-        __builtin_amdgcn_sched_barrier(0);
+        // holds it (the same value in both lane halves).
         {
             const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                                 0x38383838, 0x38383838, 0x38383838, 0x38383838};
             const f32x16 rs = mfma_fp8_32x32x64(ones, pf, f32x16{}, 127);
-            float all = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                all += rs[r];
-            lr_run += all * (1.0f / 16) * inv_fk;
+            lr_run += rs[0] * inv_fk;
         }
-        __builtin_amdgcn_sched_barrier(0);
 
         wait_vmem_all();
         __syncthreads();
@@ -306,7 +281,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
 {
     using Cfg = FwdFp8Cfg<D>;
     constexpr int kMB = Cfg::kMB;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Cfg::kBufBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[Cfg::kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -336,7 +314,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     const int nkb = (Skv + Cfg::kScaleBlock - 1) / Cfg::kScaleBlock;
 
     FwdFp8Tile<D> st;
-    st.smem = smem;
+    st.kbuf[0] = k_lds0;
+    st.kbuf[1] = k_lds1;
+    st.vbuf[0] = v_lds0;
+    st.vbuf[1] = v_lds1;
     st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     st.hh = hh;
     st.Skv = Skv;
