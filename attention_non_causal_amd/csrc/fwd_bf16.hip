@@ -30,10 +30,10 @@
 //       to k slots, so no register shuffle is needed.
 //   Software pipeline: iteration j runs the P V product of tile j-1, the K Q^T
 //   product of tile j+1 and the softmax of tile j.  The three are independent,
-//   so the 32 (d = 128) matrix instructions of an iteration alternate between
-//   the two products, and the softmax's vector instructions are spread over
-//   the same slots: the vector ALU works in the shadow of the matrix core
-//   instead of after it.  The slots are fenced (sched_barrier) so the compiler
+//   so the 32 (d = 128) matrix instructions of an iteration interleave the two
+//   products (per 16-key step: its P V instructions, then as many K Q^T ones),
+//   and the softmax's vector instructions are spread over the same slots: the
+//   vector ALU works in the shadow of the matrix core instead of after it.  The slots are fenced (sched_barrier) so the compiler
 //   keeps that order.  LDS operands are read several slots ahead.
 //   Softmax in the log2 domain: scale*log2(e) is folded into one FMA before
 //   v_exp_f32.  The weights of a whole pass over the keys are taken against one
@@ -194,7 +194,7 @@ struct FwdBf16Tile {
     f32x16 sacc[2][2];       // [parity][32-key block]: S^T of a tile
     u32x4 pf[2][4];          // [parity][16-key step]: P^T of a tile
     u32x2 vf[kVReads];       // V^T fragments of one 16-key step
-    u32x4 kf[3];             // K fragments, three in flight
+    u32x4 kf[kMB];           // K fragments of one group of K Q^T slots
     uint32_t pw[2];          // bf16 pairs of the even group of a 16-key step
     float lsum;              // sum of this lane's weights of the current tile
     float lsum_max;          // largest lsum of the pass (checked against kWeightSumLimit)
@@ -230,7 +230,7 @@ struct FwdBf16Tile {
     template <int KB, int Q>
     __device__ __forceinline__ void read_k()
     {
-        kf[Q % 3] = ld_lds16(kbuf[KB] + k_off(Q / 2) + 32 * (Q % 2) * kRow);
+        kf[Q % kMB] = ld_lds16(kbuf[KB] + k_off(Q / 2) + 32 * (Q % 2) * kRow);
     }
 
     // Transpose read E (block E/2, half E%2) of 16-key step T from V buffer VB:
@@ -362,34 +362,40 @@ struct FwdBf16Tile {
     }
 
     // Slot I of iteration parity P: one matrix instruction, the LDS reads
-    // for later slots, and a share of the softmax.
-    //   even I: O^T += V^T P^T, 16-key step t = I/(2 kMB), block mb
-    //           (P^T of the previous tile, V from buffer P^1);
-    //   odd I:  S^T += K Q^T for the next tile, k step q/2, 32-key block q%2
-    //           (K from buffer P^1).
+    // for later slots, and a share of the softmax.  Slots come in groups of
+    // 2 kMB, one per 16-key step t of the previous tile:
+    //   first kMB: O^T += V^T P^T of step t, block mb (P^T of the previous
+    //              tile, V from buffer P^1), all with the same B operand;
+    //   last kMB:  S^T += K Q^T for the next tile (K from buffer P^1), K Q^T
+    //              instructions kMB t .. kMB t + kMB-1 (k step q/2, 32-key
+    //              block q%2), pairs with the same B operand.
+    // (Grouping instructions that share an operand was +3.5% for d = 64 and
+    // neutral for d = 128 against alternating the two products.)
     template <int P, int I>
     __device__ __forceinline__ void slot()
     {
-        constexpr int v = I / 2;
-        if constexpr (I % 2 == 0) {
-            constexpr int t = v / kMB, mb = v % kMB;
+        // group t of 2 kMB slots: kMB P V instructions of 16-key step t (one
+        // P^T operand), then kMB K Q^T instructions (pairs share Q^T)
+        constexpr int t = I / (2 * kMB), i = I % (2 * kMB);
+        if constexpr (i < kMB) {
+            constexpr int mb = i;
             mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
                    pf[P ^ 1][t]);
+            // K operand of this group's K Q^T instruction i, kMB slots ahead
+            read_k<P ^ 1, kMB * t + i>();
         } else {
-            constexpr int s = v / 2, kb = v % 2;
+            constexpr int v = kMB * t + i - kMB, s = v / 2, kb = v % 2;
             if constexpr (s == 0)
-                mfma_s0(sacc[P ^ 1][kb], kf[v % 3], qf[s]);
+                mfma_s0(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
             else
-                mfma_s(sacc[P ^ 1][kb], kf[v % 3], qf[s]);
-            if constexpr (v + 2 < 2 * kSteps)
-                read_k<P ^ 1, v + 2>();
+                mfma_s(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
         }
-        // transpose read E of 16-key step t >= 1 in slot 2kMB(t-1) + E + 1, one
-        // slot after the step before has consumed fragment E
-        if constexpr (I >= 1) {
-            constexpr int t = (I - 1) / kVReads + 1, E = (I - 1) % kVReads;
-            if constexpr (t < 4)
-                read_v<P ^ 1, t, E>();
+        // V^T fragments 2mb, 2mb+1 of step t+1, one slot after step t's block
+        // mb consumed them
+        if constexpr (i >= 1 && i <= kMB && t + 1 < 4) {
+            constexpr int mb = i - 1;
+            read_v<P ^ 1, t + 1, 2 * mb>();
+            read_v<P ^ 1, t + 1, 2 * mb + 1>();
         }
         softmax_part<P, I>();
         if constexpr (I == Cfg::kCopySlotV)
@@ -442,8 +448,6 @@ struct FwdBf16Tile {
 #pragma unroll
         for (int e = 0; e < kVReads; ++e)
             vf[e] = ld_v<P ^ 1>(0, e);
-        read_k<P ^ 1, 0>();
-        read_k<P ^ 1, 1>();
         __builtin_amdgcn_sched_barrier(0);
         slots<P, 0>();
         l_run += lsum;
