@@ -43,10 +43,12 @@
 //   so far above the reference that a lane's weight sum for a tile passes
 //   2^32, the workgroup computes the exact row maxima of its key range and
 //   makes the pass again (see the kernel).
-//   LDS: two K and two V tile buffers, each its own LDS object.  Iteration j
-//   reads K(j+1), V(j-1) from one pair while K(j+2), V(j) are copied into the
-//   other; one barrier per iteration.  (Separate objects also let the compiler
-//   see that the transpose reads never alias an outstanding copy.)
+//   LDS: a ring of K and V tile buffers (four slots each for d = 128, two for
+//   d = 64), each its own LDS object.  Iteration j reads K(j+1), V(j-1) from
+//   slot j while the copies of the tiles that iteration j + kRing/2 reads go
+//   into slot j + kRing/2, last read by iteration j - kRing/2: one barrier
+//   per kRing/2 iterations.  (Separate objects also let the compiler see that
+//   the transpose reads never alias an outstanding copy.)
 //   K tile layout: rows of D bf16; the 16-byte chunk c of row r sits at chunk
 //   slot c ^ f(r), where f permutes bits of r so that the K operand read (16
 //   rows x one chunk) covers all 64 banks.  V tile layout: D/32 blocks of 32
@@ -84,6 +86,10 @@ struct FwdBf16Cfg {
     static constexpr int kCopySlotV = D == 128 ? 0 : -1;
     static constexpr int kCopySlotK = D == 128 ? 8 : -1;
     static constexpr int kVBlockBytes = kBc * 64;          // V tile: one 32-channel block
+    // K and V tile buffers each (ring slots).  d = 128: four, so that one
+    // barrier serves two iterations; d = 64: two (with two workgroups per CU
+    // the deeper ring was slower).
+    static constexpr int kRing = D == 128 ? 4 : 2;
     // Bound on one lane's sum of weights of one tile (32 weights), which keeps
     // every weight <= 2^32: O and the sums cannot overflow for |V| < 2^80.
     static constexpr float kWeightSumLimit = 0x1p32f;
@@ -178,9 +184,11 @@ struct FwdBf16Tile {
     static constexpr int kSlots = D / 4;           // matrix instructions per iteration
     static constexpr int kVReads = 2 * kMB;        // V^T transpose reads per 16-key step
     static constexpr int kPer = kSlots / 8;        // slots per group of 4 scores
+    static constexpr int kHalf = Cfg::kRing / 2;   // iterations per barrier
 
-    uint8_t* kbuf[2];
-    uint8_t* vbuf[2];
+    // K and V tile buffers (ring slots 0 .. kRing-1), each its own LDS object.
+    uint8_t* kobj[Cfg::kRing];
+    uint8_t* vobj[Cfg::kRing];
     __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
     uint32_t tok_bytes;
     int key_end, wave, hh;   // keys >= key_end are masked (the end of this block's range)
@@ -188,8 +196,8 @@ struct FwdBf16Tile {
     uint32_t k_voff;         // this lane's source offset in K copy 0 (copy i: + i * kLoadRows rows)
     uint32_t v_voff;         // this lane's source offset in V copy 0 (copy i: + kWaves/4 blocks)
     u32x4 qf[kSteps];        // bf16 operands are carried as raw 32-bit words
-    int k_addr[kSteps / 2];  // steps s and s + kSteps/2 differ in one address bit
-    uint32_t v_reg;          // LDS address of this lane's V transpose reads in V buffer 0
+    int k_addr[kSteps / 2];  // LDS address in K slot 0; steps s and s + kSteps/2 differ in one bit
+    uint32_t v_reg;          // LDS address of this lane's V transpose reads in V slot 0
     f32x16 oacc[kMB];
     f32x16 sacc[2][2];       // [parity][32-key block]: S^T of a tile
     u32x4 pf[2][4];          // [parity][16-key step]: P^T of a tile
@@ -202,9 +210,18 @@ struct FwdBf16Tile {
     float l_run;   // running sum over this lane's half of the keys
     int copy_kt;   // tile of the current iteration (for copies issued in its slots)
 
-    // Copy tile kt of K (to K buffer KB) and/or of V (to V buffer VB) into LDS;
+    // Copy tile kt of K (to K ring slot KB) and/or of V (to V slot VB) into LDS;
     // a negative buffer index skips that tensor.  Rows past the last key lie
     // outside the buffer range and read as zeros.
+    __device__ __forceinline__ uint8_t* kbuf(int R) const
+    {
+        return kobj[R];
+    }
+    __device__ __forceinline__ uint8_t* vbuf(int R) const
+    {
+        return vobj[R];
+    }
+
     template <int KB, int VB>
     __device__ __forceinline__ void copy_tile(int kt)
     {
@@ -213,35 +230,46 @@ struct FwdBf16Tile {
         for (int i = 0; i < Cfg::kLoads; ++i) {
             const int off = (i * Cfg::kWaves + wave) * 1024;
             if constexpr (KB >= 0)
-                copy16_to_lds(k_rsrc, kbuf[KB] + off, k_voff,
+                copy16_to_lds(k_rsrc, kbuf(KB) + off, k_voff,
                               soff + (uint32_t)(i * Cfg::kLoadRows) * tok_bytes);
             if constexpr (VB >= 0)
-                copy16_to_lds(v_rsrc, vbuf[VB] + off, v_voff, soff + i * (Cfg::kWaves / 4) * 64);
+                copy16_to_lds(v_rsrc, vbuf(VB) + off, v_voff, soff + i * (Cfg::kWaves / 4) * 64);
         }
     }
 
-    // LDS byte offset of the K operand of k step s (see k_addr).
+    // LDS address of the K operand of k step s in K slot 0 (see k_addr).
     __device__ __forceinline__ int k_off(int s) const
     {
         return s < kSteps / 2 ? k_addr[s] : (k_addr[s - kSteps / 2] ^ (16 * kSteps));
     }
 
-    // K operand of K Q^T step q (k step q/2, 32-key block q%2) from K buffer KB.
+    // K operand of k step s, 32-key block kb, from K ring slot KB: the per-lane
+    // address in slot 0 plus a constant (the slot's distance from slot 0 folds
+    // into the instruction's offset field).
+    template <int KB>
+    __device__ __forceinline__ u32x4 ld_k(int s, int kb) const
+    {
+        return ld_lds16(kobj[KB] + (k_off(s) - (int)lds_addr(kobj[0]) + 32 * kb * kRow));
+    }
+
+    // K operand of K Q^T step q (k step q/2, 32-key block q%2) from K ring slot KB.
     template <int KB, int Q>
     __device__ __forceinline__ void read_k()
     {
-        kf[Q % kMB] = ld_lds16(kbuf[KB] + k_off(Q / 2) + 32 * (Q % 2) * kRow);
+        kf[Q % kMB] = ld_k<KB>(Q / 2, Q % 2);
     }
 
-    // Transpose read E (block E/2, half E%2) of 16-key step T from V buffer VB:
-    // this lane's address in V buffer 0 plus a constant, written so that the
-    // constant (the buffer's distance from buffer 0, the block, the keys)
-    // folds into the instruction's offset field.
+    // Transpose read E (block E/2, half E%2) of 16-key step T from V slot VB:
+    // this lane's address in V slot 0 plus a constant, written so that the
+    // constant (the slot's distance from slot 0, the block, the keys) folds
+    // into the instruction's offset field.  (The fold needs the subtraction in
+    // the same basic block as the read: iteration() re-pins v_reg after its
+    // branch.)
     template <int VB>
     __device__ __forceinline__ u32x2 ld_v(int T, int E) const
     {
         const int c = (E / 2) * Cfg::kVBlockBytes + (16 * T + 8 * (E % 2)) * 64;
-        return ld_lds_tr16(vbuf[VB] + ((int)v_reg - (int)lds_addr(vbuf[0]) + c));
+        return ld_lds_tr16(vobj[VB] + ((int)v_reg - (int)lds_addr(vobj[0]) + c));
     }
 
     template <int VB, int T, int E>
@@ -250,7 +278,7 @@ struct FwdBf16Tile {
         vf[E] = ld_v<VB>(T, E);
     }
 
-    // The full S^T of one tile from K buffer KB into sacc[SP] (prologue only).
+    // The full S^T of one tile from K slot KB into sacc[SP] (prologue only).
     template <int KB, int SP>
     __device__ __forceinline__ void qk_tile()
     {
@@ -258,7 +286,7 @@ struct FwdBf16Tile {
         for (int s = 0; s < kSteps; ++s)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 a = ld_lds16(kbuf[KB] + k_off(s) + 32 * kb * kRow);
+                const u32x4 a = ld_k<KB>(s, kb);
                 if (s == 0)
                     mfma_s0(sacc[SP][kb], a, qf[s]);
                 else
@@ -346,12 +374,12 @@ struct FwdBf16Tile {
         return fmaxf(m, partner32(m, hh)) * scale_log2;
     }
 
-    // One step of the maximum pass: S^T of the tile kt from K buffer KB (its
-    // copy waited for), the copy of K(kt+1) into the other buffer started.
+    // One step of the maximum pass: S^T of the tile kt from K slot KB (its
+    // copy waited for), the copy of K(kt+1) into slot KB + kRing/2 started.
     template <int KB>
     __device__ __forceinline__ void max_step(int kt, float& m)
     {
-        copy_tile<KB ^ 1, -1>(kt + 1);
+        copy_tile<(KB + Cfg::kRing / 2) % Cfg::kRing, -1>(kt + 1);
         qk_tile<KB, 0>();
         const int key0 = kt * kBc;
         if (key0 + kBc > key_end)
@@ -361,28 +389,29 @@ struct FwdBf16Tile {
         __syncthreads();
     }
 
-    // Slot I of iteration parity P: one matrix instruction, the LDS reads
-    // for later slots, and a share of the softmax.  Slots come in groups of
-    // 2 kMB, one per 16-key step t of the previous tile:
+    // Slot I of the iteration that reads ring slot R (parity P = R % 2): one
+    // matrix instruction, the LDS reads for later slots, and a share of the
+    // softmax.  Slots come in groups of 2 kMB, one per 16-key step t of the
+    // previous tile:
     //   first kMB: O^T += V^T P^T of step t, block mb (P^T of the previous
-    //              tile, V from buffer P^1), all with the same B operand;
-    //   last kMB:  S^T += K Q^T for the next tile (K from buffer P^1), K Q^T
+    //              tile, V from slot R), all with the same B operand;
+    //   last kMB:  S^T += K Q^T for the next tile (K from slot R), K Q^T
     //              instructions kMB t .. kMB t + kMB-1 (k step q/2, 32-key
     //              block q%2), pairs with the same B operand.
     // (Grouping instructions that share an operand was +3.5% for d = 64 and
     // neutral for d = 128 against alternating the two products.)
-    template <int P, int I>
+    template <int R, int I>
     __device__ __forceinline__ void slot()
     {
-        // group t of 2 kMB slots: kMB P V instructions of 16-key step t (one
-        // P^T operand), then kMB K Q^T instructions (pairs share Q^T)
+        constexpr int P = R % 2;
+        constexpr int W = (R + kHalf) % Cfg::kRing;  // ring slot this iteration's copies fill
         constexpr int t = I / (2 * kMB), i = I % (2 * kMB);
         if constexpr (i < kMB) {
             constexpr int mb = i;
             mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
                    pf[P ^ 1][t]);
             // K operand of this group's K Q^T instruction i, kMB slots ahead
-            read_k<P ^ 1, kMB * t + i>();
+            read_k<R, kMB * t + i>();
         } else {
             constexpr int v = kMB * t + i - kMB, s = v / 2, kb = v % 2;
             if constexpr (s == 0)
@@ -394,36 +423,38 @@ struct FwdBf16Tile {
         // mb consumed them
         if constexpr (i >= 1 && i <= kMB && t + 1 < 4) {
             constexpr int mb = i - 1;
-            read_v<P ^ 1, t + 1, 2 * mb>();
-            read_v<P ^ 1, t + 1, 2 * mb + 1>();
+            read_v<R, t + 1, 2 * mb>();
+            read_v<R, t + 1, 2 * mb + 1>();
         }
         softmax_part<P, I>();
         if constexpr (I == Cfg::kCopySlotV)
-            copy_tile<-1, P>(copy_kt);
+            copy_tile<-1, W>(copy_kt + kHalf - 1);
         if constexpr (I == Cfg::kCopySlotK)
-            copy_tile<P, -1>(copy_kt + 2);
+            copy_tile<W, -1>(copy_kt + kHalf + 1);
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    template <int P, int I>
+    template <int R, int I>
     __device__ __forceinline__ void slots()
     {
         if constexpr (I < kSlots) {
-            slot<P, I>();
-            slots<P, I + 1>();
+            slot<R, I>();
+            slots<R, I + 1>();
         }
     }
 
-    // The P V product of the last tile alone (in place of a whole iteration
-    // P, with the same operands: P^T from pf[P^1], V from buffer P^1).
-    template <int P>
-    __device__ __forceinline__ void drain()
+    // The P V product of the last tile alone (after an even number of
+    // iterations: P^T in pf[1], V in ring slot 0 or, for four slots, 2, as
+    // vb says).
+    __device__ __forceinline__ void drain(const uint8_t* vb)
     {
+        constexpr int P = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int e = 0; e < kVReads; ++e)
-                vf[e] = ld_v<P ^ 1>(t, e);
+                vf[e] = ld_lds_tr16(vb + ((int)v_reg - (int)lds_addr(vobj[0]) + (e / 2) * Cfg::kVBlockBytes +
+                                          (16 * t + 8 * (e % 2)) * 64));
 #pragma unroll
             for (int mb = 0; mb < kMB; ++mb)
                 mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
@@ -431,29 +462,38 @@ struct FwdBf16Tile {
         }
     }
 
-    // Iteration kt (parity P = kt % 2): P V of tile kt-1, K Q^T of tile kt+1,
-    // softmax of tile kt; copies K(kt+2) and V(kt) into buffers P.
-    template <int P>
+    // Iteration kt, reading ring slot R (kt - first tile = R mod kRing): P V
+    // of tile kt-1 (V there), K Q^T of tile kt+1 (K there), softmax of tile
+    // kt; copies V(kt + kHalf-1), K(kt + kHalf+1) into ring slot R + kHalf,
+    // which iteration kt - kHalf read last.  Every kHalf-th iteration waits
+    // for its copies and ends with the one barrier of its group.
+    template <int R>
     __device__ __forceinline__ void iteration(int kt)
     {
+        constexpr int P = R % 2;
+        constexpr int W = (R + kHalf) % Cfg::kRing;
         copy_kt = kt;
         if constexpr (Cfg::kCopySlotV < 0)
-            copy_tile<-1, P>(kt);
+            copy_tile<-1, W>(kt + kHalf - 1);
         if constexpr (Cfg::kCopySlotK < 0)
-            copy_tile<P, -1>(kt + 2);
+            copy_tile<W, -1>(kt + kHalf + 1);
         const int key0 = kt * kBc;
         if (key0 + kBc > key_end)
             mask_tile<P>(key0);
-        // operands of the first slots
+        // re-pinned here, in the block of all of this iteration's V reads:
+        // then its distance from slot R folds into their offset fields
+        pin(v_reg);
 #pragma unroll
         for (int e = 0; e < kVReads; ++e)
-            vf[e] = ld_v<P ^ 1>(0, e);
+            vf[e] = ld_v<R>(0, e);
         __builtin_amdgcn_sched_barrier(0);
-        slots<P, 0>();
+        slots<R, 0>();
         l_run += lsum;
         lsum_max = fmaxf(lsum_max, lsum);
-        wait_vmem_all();
-        __syncthreads();
+        if constexpr (R % kHalf == kHalf - 1) {
+            wait_vmem_all();
+            __syncthreads();
+        }
     }
 };
 
@@ -474,10 +514,18 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     using Cfg = FwdBf16Cfg<D>;
     constexpr int kMB = Cfg::kMB;
     constexpr int kRow = Cfg::kRowBytes;
+    constexpr int kRing = Cfg::kRing;
+    constexpr int kHalf = kRing / 2;
+    // (slots 2 and 3 are referenced only with four slots; unreferenced LDS
+    // objects take no space)
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds3[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[Cfg::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds3[Cfg::kTileBytes];
     __shared__ int wave_over[Cfg::kWaves];
 
     const int tid = threadIdx.x;
@@ -506,10 +554,16 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     const long tok = (long)H * D;  // elements between consecutive tokens
 
     FwdBf16Tile<D> st;
-    st.kbuf[0] = k_lds0;
-    st.kbuf[1] = k_lds1;
-    st.vbuf[0] = v_lds0;
-    st.vbuf[1] = v_lds1;
+    st.kobj[0] = k_lds0;
+    st.kobj[1] = k_lds1;
+    st.vobj[0] = v_lds0;
+    st.vobj[1] = v_lds1;
+    if constexpr (kRing == 4) {
+        st.kobj[2] = k_lds2;
+        st.kobj[3] = k_lds3;
+        st.vobj[2] = v_lds2;
+        st.vobj[3] = v_lds3;
+    }
     st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     st.hh = hh;
     st.key_end = min(kt1 * Cfg::kBc, Skv);
@@ -538,11 +592,21 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
         st.k_voff = (uint32_t)r * st.tok_bytes + swz_slot<D>(r, p % Cfg::kChunks) * 16;
         st.v_voff = (uint32_t)((p / 4) % 64) * st.tok_bytes + ((p / 256) * 4 + p % 4) * 16;
     }
-    // A pass starts with K(kt0), K(kt0+1) for the first two K Q^T products and
-    // V(kt0+1) in V buffer 1, where the first iteration's P V (with P = 0)
-    // reads finite values.  (The first pass's copies overlap the Q loads.)
-    st.template copy_tile<0, -1>(kt0);
-    st.template copy_tile<1, 1>(kt0 + 1);
+    // A pass starts with what its first kHalf iterations read: K(kt0) in the
+    // last ring slot (the prologue's K Q^T), K(kt0+1) .. K(kt0+kHalf) in
+    // slots 0 .. kHalf-1, V(kt0) in slot 1 when four slots, and V(kt0) in
+    // slot 0, where the first iteration's P V (with P = 0) reads finite
+    // values.  (The first pass's copies overlap the Q loads.)
+    auto pass_copies = [&]() {
+        st.template copy_tile<kRing - 1, -1>(kt0);
+        st.template copy_tile<0, -1>(kt0 + 1);
+        if constexpr (kRing == 4) {
+            st.template copy_tile<1, -1>(kt0 + 2);
+            st.template copy_tile<-1, 1>(kt0);
+        }
+        st.template copy_tile<-1, 0>(kt0);
+    };
+    pass_copies();
 
     const int q_row = qt * Cfg::kBr + st.wave * 32 + n;
     if (q_row < Sq) {
@@ -571,7 +635,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     // half-wave cover 4 keys x 64 contiguous bytes: all 64 banks once.)
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-        st.k_addr[s] = lds_byte<D>(n, 16 * s + 8 * hh);
+        st.k_addr[s] = lds_addr(k_lds0) + lds_byte<D>(n, 16 * s + 8 * hh);
     st.v_reg = lds_addr(v_lds0) + (4 * hh + ((lane & 15) >> 2)) * 64 +
                (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     pin(st.v_reg);
@@ -597,26 +661,46 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
 
         wait_vmem_all();
         __syncthreads();
-        st.template qk_tile<0, 0>();
+        st.template qk_tile<kRing - 1, 0>();
         if (pass == 0) {
             if (kt0 * Cfg::kBc + Cfg::kBc > st.key_end)
                 st.template mask_tile<0>(kt0 * Cfg::kBc);
             st.m_used = st.template tile_max<0>();
         }
-        __syncthreads();  // K buffer 0 is refilled by the first iteration
+        __syncthreads();  // the last ring slot is refilled by iteration kHalf-1
 
-        // One iteration per tile of the range, in pairs (the buffer index is
-        // compile-time), then the last tile's P V: by one more iteration if
-        // the count is odd (its own tile lies past the range: all keys
-        // masked, weights 0), else by drain().
+        // One iteration per tile of the range, unrolled over the ring slots
+        // (the slot indices are compile-time), then the last tile's P V: by
+        // one more iteration if the count is odd (its own tile lies past the
+        // range: all keys masked, weights 0), else by drain().
         const int n_it = kt1 - kt0;
+        const int n_pad = (n_it + 1) & ~1;
         int i = 0;
-        for (; i < n_it; i += 2) {
-            st.template iteration<0>(kt0 + i);
-            st.template iteration<1>(kt0 + i + 1);
+        if constexpr (kRing == 4) {
+            for (; i + 4 <= n_pad; i += 4) {
+                st.template iteration<0>(kt0 + i);
+                st.template iteration<1>(kt0 + i + 1);
+                st.template iteration<2>(kt0 + i + 2);
+                st.template iteration<3>(kt0 + i + 3);
+            }
+            if (i < n_pad) {
+                st.template iteration<0>(kt0 + i);
+                st.template iteration<1>(kt0 + i + 1);
+                i += 2;
+            }
+        } else {
+            for (; i < n_pad; i += 2) {
+                st.template iteration<0>(kt0 + i);
+                st.template iteration<1>(kt0 + i + 1);
+            }
         }
+        // the last iteration's K Q^T result (of a tile past the range) is
+        // dead: hold its registers until that matrix instruction is done
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            vgpr_wait(st.sacc[0][kb]);
         if (i == n_it)
-            st.template drain<0>();
+            st.drain(i % kRing == 0 ? st.vobj[0] : st.vobj[kRing - 2]);
 
         if (lane == 0)
             wave_over[st.wave] = __builtin_amdgcn_ballot_w64(st.lsum_max > Cfg::kWeightSumLimit) != 0;
@@ -636,11 +720,10 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
         const int n_mx = (kt1 - kt0 + 1) & ~1;
         for (int i = 0; i < n_mx; i += 2) {
             st.template max_step<0>(kt0 + i, m);
-            st.template max_step<1>(kt0 + i + 1, m);
+            st.template max_step<kHalf>(kt0 + i + 1, m);
         }
         st.m_used = m;
-        st.template copy_tile<0, -1>(kt0);
-        st.template copy_tile<1, 1>(kt0 + 1);
+        pass_copies();
     }
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
