@@ -33,8 +33,12 @@
 //   so the 32 (d = 128) matrix instructions of an iteration interleave the two
 //   products (per 16-key step: its P V instructions, then as many K Q^T ones),
 //   and the softmax's vector instructions are spread over the same slots: the
-//   vector ALU works in the shadow of the matrix core instead of after it.  The slots are fenced (sched_barrier) so the compiler
-//   keeps that order.  LDS operands are read several slots ahead.
+//   vector ALU works in the shadow of the matrix core instead of after it.
+//   The slots are fenced (sched_barrier) so the compiler keeps that order.
+//   LDS operands are read several slots ahead; the last group's K operands
+//   are read during the group before, and the first V operands of iteration
+//   j+1 during the last group of iteration j, so that no iteration starts by
+//   waiting on LDS.
 //   Softmax in the log2 domain: scale*log2(e) is folded into one FMA before
 //   v_exp_f32.  The weights of a whole pass over the keys are taken against one
 //   reference maximum (the first tile's row maximum): the final O / sum and LSE
@@ -47,8 +51,11 @@
 //   d = 64), each its own LDS object.  Iteration j reads K(j+1), V(j-1) from
 //   slot j while the copies of the tiles that iteration j + kRing/2 reads go
 //   into slot j + kRing/2, last read by iteration j - kRing/2: one barrier
-//   per kRing/2 iterations.  (Separate objects also let the compiler see that
-//   the transpose reads never alias an outstanding copy.)
+//   per kRing/2 iterations.  It sits before the last group of K Q^T
+//   instructions (whose operands are in registers by then), once all LDS
+//   reads of the iteration are done, so the next iteration's first reads
+//   overlap those matrix instructions.  (Separate objects also let the
+//   compiler see that the transpose reads never alias an outstanding copy.)
 //   K tile layout: rows of D bf16; the 16-byte chunk c of row r sits at chunk
 //   slot c ^ f(r), where f permutes bits of r so that the K operand read (16
 //   rows x one chunk) covers all 64 banks.  V tile layout: D/32 blocks of 32
@@ -90,6 +97,8 @@ struct FwdBf16Cfg {
     // barrier serves two iterations; d = 64: two (with two workgroups per CU
     // the deeper ring was slower).
     static constexpr int kRing = D == 128 ? 4 : 2;
+    // Softmax sums and bf16 pairs one slot after the weights (see softmax_part).
+    static constexpr bool kFoldLater = D == 128;
     // Bound on one lane's sum of weights of one tile (32 weights), which keeps
     // every weight <= 2^32: O and the sums cannot overflow for |V| < 2^80.
     static constexpr float kWeightSumLimit = 0x1p32f;
@@ -203,7 +212,7 @@ struct FwdBf16Tile {
     u32x4 pf[2][4];          // [parity][16-key step]: P^T of a tile
     u32x2 vf[kVReads];       // V^T fragments of one 16-key step
     u32x4 kf[kMB];           // K fragments of one group of K Q^T slots
-    uint32_t pw[2];          // bf16 pairs of the even group of a 16-key step
+    uint32_t pw[2];          // bf16 pairs of the even group of a 16-key step (d = 64)
     float lsum;              // sum of this lane's weights of the current tile
     float lsum_max;          // largest lsum of the pass (checked against kWeightSumLimit)
     float m_used;  // reference maximum (scale*log2(e) units) of the weights, fixed per pass
@@ -299,37 +308,39 @@ struct FwdBf16Tile {
 
     // Softmax of the tile in sacc[P], vector work of slot I.  The weights are
     // 2^(scale*log2(e)*s - m_used) with m_used fixed for the whole pass (see
-    // the kernel), so a tile needs no maximum of its own.  8 groups of 4
-    // scores, group G (32-key block G/4) in slots kPer*G .. kPer*G + kPer-1:
-    // the weights (in place) of 4/kPer scores per slot, then in the group's
-    // last slot their sum and bf16 pairs.  Block 1's groups start at slot
-    // 4*kPer >= 2, two matrix instructions after its last K Q^T step.
+    // the kernel), so a tile needs no maximum of its own.  Score w is register
+    // w%16 of 32-key block w/16; slot I computes weights kW*I .. kW*I + kW-1
+    // in place (block 1's from slot 16/kW >= 8 on, well after its last K Q^T
+    // step).  Their sum and bf16 pairs:
+    //   d = 128 (kFoldLater): one slot later (fold), so that no instruction
+    //     waits on an exponential of its own slot;
+    //   d = 64: per group of 4 weights, in the group's last slot (faster there).
+    static constexpr int kW = 32 / kSlots;  // weights per slot
+
     template <int P, int I>
     __device__ __forceinline__ void softmax_part()
     {
-        constexpr int G = I / kPer;  // group of 4 scores
-        constexpr int sub = I % kPer;
-        constexpr int kb = G / 4;
-        constexpr int r0 = 4 * (G % 4);
-        constexpr int kW = 4 / kPer;  // weights per slot
         // re-pinned each slot, so that this slot's weights cannot be hoisted
         // into an earlier one
         pin(m_used);
-        f32x16& s = sacc[P][kb];
 #pragma unroll
-        for (int r = r0 + kW * sub; r < r0 + kW * (sub + 1); ++r) {
-            float e = exp2_fast(__builtin_fmaf(s[r], scale_log2, -m_used));
+        for (int w = kW * I; w < kW * (I + 1); ++w) {
+            float e = exp2_fast(__builtin_fmaf(sacc[P][w / 16][w % 16], scale_log2, -m_used));
             pin(e);
-            s[r] = e;
+            sacc[P][w / 16][w % 16] = e;
         }
-        if constexpr (sub == kPer - 1) {
+        if constexpr (Cfg::kFoldLater) {
+            if constexpr (I > 0)
+                fold<P, I - 1>();
+        } else if constexpr ((kW * (I + 1)) % 4 == 0) {
+            // group of weights w0 .. w0+3 complete: its sum, and its two bf16
+            // pairs (words 2(G%2), 2(G%2)+1 of the P^T fragment of step t)
+            constexpr int w0 = kW * (I + 1) - 4, G = w0 / 4, kb = w0 / 16, r0 = w0 % 16;
+            const f32x16& s = sacc[P][kb];
             const float g = (s[r0] + s[r0 + 1]) + (s[r0 + 2] + s[r0 + 3]);
             lsum = G == 0 ? g : lsum + g;
             pin(lsum);
-            // P^T fragment of 16-key step t = registers 8(t%2)..+7 of block
-            // t/2: the even group gives its first two words, the odd group
-            // the last two
-            constexpr int t = 2 * kb + (G % 4) / 2;
+            constexpr int t = w0 / 8;
             if constexpr (G % 2 == 0) {
                 pw[0] = pack_bf16x2(s[r0], s[r0 + 1]);
                 pw[1] = pack_bf16x2(s[r0 + 2], s[r0 + 3]);
@@ -340,6 +351,24 @@ struct FwdBf16Tile {
                            pack_bf16x2(s[r0 + 2], s[r0 + 3])};
                 pin(v);
                 pf[P][t] = v;
+            }
+        }
+    }
+
+    // The weights of slot J into lsum and into P^T: the fragment of 16-key
+    // step t holds registers 8(t%2) .. 8(t%2)+7 of block t/2 as bf16 pairs.
+    template <int P, int J>
+    __device__ __forceinline__ void fold()
+    {
+#pragma unroll
+        for (int w = kW * J; w < kW * (J + 1); ++w) {
+            const float e = sacc[P][w / 16][w % 16];
+            lsum = w == 0 ? e : lsum + e;
+            pin(lsum);
+            if (w % 2 == 1) {
+                uint32_t pk = pack_bf16x2(sacc[P][w / 16][w % 16 - 1], e);
+                pin(pk);
+                pf[P][w / 8][(w % 8) / 2] = pk;
             }
         }
     }
@@ -406,18 +435,41 @@ struct FwdBf16Tile {
         constexpr int P = R % 2;
         constexpr int W = (R + kHalf) % Cfg::kRing;  // ring slot this iteration's copies fill
         constexpr int t = I / (2 * kMB), i = I % (2 * kMB);
+        if constexpr (I == kSlots - kMB) {
+            // The group's barrier: every wave's copies so far have landed (so
+            // the slots of the next kHalf iterations hold their tiles) and
+            // every wave has finished its reads of this group's slots (the
+            // last ones were issued in the group before, and the barrier
+            // waits for them), which later copies overwrite.  Then step 0 of
+            // the next iteration's V^T fragments.
+            if constexpr (R % kHalf == kHalf - 1) {
+                wait_vmem_all();
+                __syncthreads();
+            }
+#pragma unroll
+            for (int e = 0; e < kVReads; ++e)
+                vf[e] = ld_v<(R + 1) % Cfg::kRing>(0, e);
+        }
         if constexpr (i < kMB) {
             constexpr int mb = i;
             mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
                    pf[P ^ 1][t]);
             // K operand of this group's K Q^T instruction i, kMB slots ahead
-            read_k<R, kMB * t + i>();
+            // (last group: read in the group before)
+            if constexpr (t < 3)
+                read_k<R, kMB * t + i>();
+            if constexpr (t == 3 && i == 0)
+                read_k<R, kMB * 3 + kMB - 1>();
         } else {
             constexpr int v = kMB * t + i - kMB, s = v / 2, kb = v % 2;
             if constexpr (s == 0)
                 mfma_s0(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
             else
                 mfma_s(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
+            // K operands of the last group, one slot after their registers'
+            // last use (the last one in the last group's first slot)
+            if constexpr (t == 2 && i > kMB)
+                read_k<R, kMB * 3 + (i - kMB - 1)>();
         }
         // V^T fragments 2mb, 2mb+1 of step t+1, one slot after step t's block
         // mb consumed them
@@ -466,7 +518,9 @@ struct FwdBf16Tile {
     // of tile kt-1 (V there), K Q^T of tile kt+1 (K there), softmax of tile
     // kt; copies V(kt + kHalf-1), K(kt + kHalf+1) into ring slot R + kHalf,
     // which iteration kt - kHalf read last.  Every kHalf-th iteration waits
-    // for its copies and ends with the one barrier of its group.
+    // for the copies and holds the one barrier of its group (in the slot
+    // program, see slot()).  On entry vf holds step 0 of this iteration's V^T
+    // fragments, read by the iteration before (or before the first one).
     template <int R>
     __device__ __forceinline__ void iteration(int kt)
     {
@@ -483,17 +537,12 @@ struct FwdBf16Tile {
         // re-pinned here, in the block of all of this iteration's V reads:
         // then its distance from slot R folds into their offset fields
         pin(v_reg);
-#pragma unroll
-        for (int e = 0; e < kVReads; ++e)
-            vf[e] = ld_v<R>(0, e);
         __builtin_amdgcn_sched_barrier(0);
         slots<R, 0>();
+        if constexpr (Cfg::kFoldLater)
+            fold<P, kSlots - 1>();
         l_run += lsum;
         lsum_max = fmaxf(lsum_max, lsum);
-        if constexpr (R % kHalf == kHalf - 1) {
-            wait_vmem_all();
-            __syncthreads();
-        }
     }
 };
 
@@ -668,6 +717,11 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
             st.m_used = st.template tile_max<0>();
         }
         __syncthreads();  // the last ring slot is refilled by iteration kHalf-1
+        // step 0 of the first iteration's V^T fragments (later iterations read
+        // theirs in the iteration before)
+#pragma unroll
+        for (int e = 0; e < 2 * kMB; ++e)
+            st.vf[e] = st.template ld_v<0>(0, e);
 
         // One iteration per tile of the range, unrolled over the ring slots
         // (the slot indices are compile-time), then the last tile's P V: by
