@@ -35,10 +35,11 @@
 //   and the softmax's vector instructions are spread over the same slots: the
 //   vector ALU works in the shadow of the matrix core instead of after it.
 //   The slots are fenced (sched_barrier) so the compiler keeps that order.
-//   LDS operands are read several slots ahead; the last group's K operands
-//   are read during the group before, and the first V operands of iteration
-//   j+1 during the last group of iteration j, so that no iteration starts by
-//   waiting on LDS.
+//   LDS operands are read several slots ahead: V^T fragments one 16-key step
+//   ahead, K operands during the group of slots before (d = 64: the last
+//   group's; the others kMB slots ahead), and the first V^T fragments of
+//   iteration j+1 during the last group of iteration j, so that no iteration
+//   starts by waiting on LDS.
 //   Softmax in the log2 domain: scale*log2(e) is folded into one FMA before
 //   v_exp_f32.  The weights of a whole pass over the keys are taken against one
 //   reference maximum (the first tile's row maximum): the final O / sum and LSE
@@ -99,6 +100,9 @@ struct FwdBf16Cfg {
     static constexpr int kRing = D == 128 ? 4 : 2;
     // Softmax sums and bf16 pairs one slot after the weights (see softmax_part).
     static constexpr bool kFoldLater = D == 128;
+    // K operands read a whole group of slots ahead (see slot()).  Both were
+    // faster for d = 128 and slower for d = 64.
+    static constexpr bool kKAhead = D == 128;
     // Bound on one lane's sum of weights of one tile (32 weights), which keeps
     // every weight <= 2^32: O and the sums cannot overflow for |V| < 2^80.
     static constexpr float kWeightSumLimit = 0x1p32f;
@@ -266,6 +270,16 @@ struct FwdBf16Tile {
     __device__ __forceinline__ void read_k()
     {
         kf[Q % kMB] = ld_k<KB>(Q / 2, Q % 2);
+    }
+
+    // K operands 0 .. kMB-2 of the first group of K Q^T slots from slot KB.
+    template <int KB, int J = 0>
+    __device__ __forceinline__ void read_ks()
+    {
+        if constexpr (J < kMB - 1) {
+            read_k<KB, J>();
+            read_ks<KB, J + 1>();
+        }
     }
 
     // Transpose read E (block E/2, half E%2) of 16-key step T from V slot VB:
@@ -454,21 +468,35 @@ struct FwdBf16Tile {
             constexpr int mb = i;
             mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
                    pf[P ^ 1][t]);
-            // K operand of this group's K Q^T instruction i, kMB slots ahead
-            // (last group: read in the group before)
-            if constexpr (t < 3)
-                read_k<R, kMB * t + i>();
-            if constexpr (t == 3 && i == 0)
-                read_k<R, kMB * 3 + kMB - 1>();
+            if constexpr (Cfg::kKAhead) {
+                // K operand of this group's last K Q^T instruction (the others
+                // were read during the group before)
+                if constexpr (i == 0)
+                    read_k<R, kMB * t + kMB - 1>();
+            } else {
+                // K operand of this group's K Q^T instruction i, kMB slots
+                // ahead (last group: read in the group before)
+                if constexpr (t < 3)
+                    read_k<R, kMB * t + i>();
+                if constexpr (t == 3 && i == 0)
+                    read_k<R, kMB * 3 + kMB - 1>();
+            }
         } else {
             constexpr int v = kMB * t + i - kMB, s = v / 2, kb = v % 2;
             if constexpr (s == 0)
                 mfma_s0(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
             else
                 mfma_s(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
-            // K operands of the last group, one slot after their registers'
-            // last use (the last one in the last group's first slot)
-            if constexpr (t == 2 && i > kMB)
+            // K operands of the next group (kKAhead; the last group: of the
+            // next iteration's first group, from its ring slot), else of the
+            // last group only, one slot after their registers' last use
+            if constexpr (Cfg::kKAhead && i > kMB) {
+                if constexpr (t < 3)
+                    read_k<R, kMB * (t + 1) + (i - kMB - 1)>();
+                else
+                    read_k<(R + 1) % Cfg::kRing, i - kMB - 1>();
+            }
+            if constexpr (!Cfg::kKAhead && t == 2 && i > kMB)
                 read_k<R, kMB * 3 + (i - kMB - 1)>();
         }
         // V^T fragments 2mb, 2mb+1 of step t+1, one slot after step t's block
@@ -722,6 +750,9 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
 #pragma unroll
         for (int e = 0; e < 2 * kMB; ++e)
             st.vf[e] = st.template ld_v<0>(0, e);
+        // and (kKAhead) the K operands of its first group, but the last
+        if constexpr (Cfg::kKAhead)
+            st.template read_ks<0>();
 
         // One iteration per tile of the range, unrolled over the ring slots
         // (the slot indices are compile-time), then the last tile's P V: by
