@@ -14,6 +14,10 @@ trained weights):
 * ``flux_fp8``  as ``flux``, then 1% of the H*d channels of each of Q, K, V
                 (31 channels, drawn independently per tensor) multiplied by 8
                 across all tokens, before e4m3 quantisation
+* ``flux_h3``   as ``flux`` with H3: what each GPU runs when 8-way Ulysses
+                shards the 24 heads ("xDiT 项目概述" sec. 3.2.2: the Ulysses
+                dimension splits by heads; sec. 3.2.3 suggests degree 8 on fast
+                links)
 * ``wan_ring``  B1 H40 d128, a 21x30x52 = 32760-token video sequence seen by one
                 of four ring ranks: 8190 local queries against all 32760 keys,
                 handled as 4 KV chunks of 8190 whose partials are merged
@@ -87,6 +91,10 @@ WORKLOADS = {
                          outlier_frac=0.01,
                          description="FLUX-like shape, e4m3 per-(head,128-token) scales, "
                                      "1% channels x8"),
+    # the shape each GPU runs under 8-way Ulysses (24 heads / 8)
+    "flux_h3": Workload("flux_h3", 1, 3, 128, 16896, 16896, qk_norm=True,
+                        description="FLUX-like shape, one GPU's share of 8-way Ulysses: "
+                                    "B1 H3 d128 S16896 bf16"),
     "wan_ring": Workload("wan_ring", 1, 40, 128, 8190, 32760, n_chunks=4,
                          description="Wan-like video, one ring rank's share: Sq8190 vs "
                                      "Skv32760 in 4 chunks + merge"),

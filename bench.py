@@ -234,7 +234,7 @@ def run_extras(dev, steps, warmup):
     from attention_non_causal_amd import _lib, functional as F
     from attention_non_causal_amd import workloads as wl
     res = {}
-    for name in ("tiny", "sd3"):
+    for name in ("tiny", "sd3", "flux_h3"):
         W = wl.WORKLOADS[name]
         g = wl.generate(W)
         q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)

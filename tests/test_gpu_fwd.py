@@ -258,7 +258,8 @@ def test_noncurrent_stream():
 
 # ------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("name,n_rows", [("tiny", None), ("sd3", 48), ("flux", 24)])
+@pytest.mark.parametrize("name,n_rows", [("tiny", None), ("sd3", 48), ("flux", 24),
+                                         ("flux_h3", 48)])
 def test_workload_parity(name, n_rows):
     W = wl.WORKLOADS[name]
     say(f"workload {name}: generating inputs")
