@@ -58,7 +58,11 @@ def test_fwd_small_full_compare(B, H, Sq, Skv, d):
     compare(o, l, o_ref, l_ref, o_tol=_gpu.few_key_o_tol(v), what=f"B{B}H{H}Sq{Sq}Skv{Skv}d{d}")
 
 
-@pytest.mark.parametrize("Skv", [1, 2, 63, 64, 65, 127, 128, 129, 255, 257])
+# 1 .. 10 key tiles: with four LDS ring slots (d = 128) the loop runs groups
+# of four iterations, then possibly a pair, then the last tile's P V either
+# alone (from slot 0 or 2) or by one more iteration: 6, 8 and 10 tiles (321,
+# 449..512, 577) take the remaining combinations
+@pytest.mark.parametrize("Skv", [1, 2, 63, 64, 65, 127, 128, 129, 255, 257, 321, 449, 512, 577])
 @pytest.mark.parametrize("d", [64, 128])
 def test_fwd_key_length_sweep(Skv, d):
     say(f"fwd Skv sweep Skv{Skv} d{d}")
