@@ -49,6 +49,7 @@ COMMON_FLAGS = [
 # input gives a NaN result either way).
 FILE_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+    "fwd_fp8.hip": ["-fno-honor-nans"],
 }
 
 

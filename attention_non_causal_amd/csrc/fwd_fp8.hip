@@ -97,7 +97,11 @@ __device__ __forceinline__ i32x8 tr8_read4(const uint8_t* p)
 // Pack 4 fp32 into 4 e4m3 bytes (round to nearest even; inputs <= 448).
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // both halves are written: the old value of the first is irrelevant (an
+    // uninitialised register, so the compiler does not zero it first)
+    int w;
+    asm volatile("" : "=v"(w));
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -125,6 +129,9 @@ struct FwdFp8Tile {
     float m_used;  // log2-domain maximum the weights are taken against
     float l_run;   // running sum of unrounded weights over this lane's keys
     float lr_run;  // running sum of the e4m3-rounded weights over all keys
+    i32x8 ones;    // all-ones e4m3 operand of the rounded-weight sums
+    f32x16 rs;     // the last tile's rounded-weight sums (added at the next step)
+    float rs_inv;  // and their 1 / (f K)
 
     template <int BUF>
     __device__ __forceinline__ void issue(int kt_next)
@@ -150,12 +157,23 @@ struct FwdFp8Tile {
         }
     }
 
+    // The previous tile's rounded-weight sum into lr_run (read one step late,
+    // so that no instruction waits on that matrix instruction).
+    __device__ __forceinline__ void add_rs()
+    {
+        // rs is held (all 16 registers) up to here, so none of them is handed
+        // to other values while that matrix instruction may still write it
+        asm volatile("" ::"v"(rs));
+        lr_run += rs[0] * rs_inv;
+    }
+
     template <int BUF>
     __device__ __forceinline__ void step(int kt)
     {
         const int key0 = kt * kBc;
         if (kt + 1 < kt_end)
             issue<BUF ^ 1>(kt + 1);
+        add_rs();
 
         // block scales of this key tile (uniform): both lie in block key0/128
         const int kblk = key0 / Cfg::kScaleBlock;
@@ -178,6 +196,11 @@ struct FwdFp8Tile {
                 a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
                 sacc[kb] = mfma_fp8_32x32x64(a, qf[s], sacc[kb], 127);
             }
+        // V^T operands of this tile, read while the K Q^T instructions run
+        i32x8 va[kMB];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+            va[mb] = tr8_read4<16 * D>(vbuf[BUF] + v_addr[mb]);
         if (key0 + kBc > Skv) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -245,19 +268,13 @@ struct FwdFp8Tile {
 
         // O^T += V8^T P''^T, P'' carrying the 2^e part of the V block scale
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-            const i32x8 va = tr8_read4<16 * D>(vbuf[BUF] + v_addr[mb]);
-            oacc[mb] = mfma_fp8_32x32x64(va, pf, oacc[mb], vexp);
-        }
+        for (int mb = 0; mb < kMB; ++mb)
+            oacc[mb] = mfma_fp8_32x32x64(va[mb], pf, oacc[mb], vexp);
 
         // Sum of the rounded weights of this tile: every row of ones^T P''^T
         // holds it (the same value in both lane halves).
-        {
-            const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                                0x38383838, 0x38383838, 0x38383838, 0x38383838};
-            const f32x16 rs = mfma_fp8_32x32x64(ones, pf, f32x16{}, 127);
-            lr_run += rs[0] * inv_fk;
-        }
+        rs = mfma_fp8_32x32x64(ones, pf, f32x16{}, 127);
+        rs_inv = inv_fk;
 
         wait_vmem_all();
         __syncthreads();
@@ -381,6 +398,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
     st.m_used = -INFINITY;
     st.l_run = 0.f;
     st.lr_run = 0.f;
+    st.rs = f32x16{};
+    st.rs_inv = 0.f;
+    // e4m3 1.0 in every byte, placed in registers once for the whole kernel
+    st.ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                    0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    asm volatile("" : "+v"(st.ones));
 
     wait_vmem_all();
     __syncthreads();
@@ -390,6 +413,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         if (kt + 1 < kt1)
             st.template step<1>(kt + 1);
     }
+    st.add_rs();
 
     const float l_tot = st.l_run + partner32(st.l_run, hh);
     const float inv = 1.f / (st.lr_run * Cfg::kPScale);
