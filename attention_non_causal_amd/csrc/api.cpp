@@ -121,14 +121,17 @@ int check_fwd_shape(int B, int H, int Sq, int Skv, int d, int dtype)
     return DIT_OK;
 }
 
-// dit_attn_fwd and dit_attn_fwd_ws; with_ws selects the split launch.
+// dit_attn_fwd, dit_attn_fwd_ws and dit_attn_fwd_acc; with_ws selects the
+// split launch, acc the merge into the running result held in o, lse.
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int Sq, int Skv, int d, float scale, int dtype, bool with_ws, void* ws,
-             size_t ws_bytes, hipStream_t stream)
+             size_t ws_bytes, bool acc, hipStream_t stream)
 {
     if (!q || !k || !v || !o || !lse)
         return DIT_ERR_NULL;
     if (dtype != DIT_DTYPE_BF16 && dtype != DIT_DTYPE_FP8_E4M3)
+        return DIT_ERR_UNSUPPORTED;
+    if (acc && dtype != DIT_DTYPE_BF16)
         return DIT_ERR_UNSUPPORTED;
     if (d != 64 && d != 128)
         return DIT_ERR_UNSUPPORTED;
@@ -196,6 +199,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.Skv = Skv;
     a.d = d;
     a.scale = scale;
+    a.acc = acc ? 1 : 0;
 
     dit::FwdSplit split = {};
     if (with_ws) {
@@ -237,7 +241,8 @@ extern "C" {
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int Sq, int Skv, int d, float scale, int dtype, hipStream_t stream)
 {
-    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, false, nullptr, 0, stream);
+    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, false, nullptr, 0, false,
+                    stream);
 }
 
 int dit_attn_fwd_workspace_size(int B, int H, int Sq, int Skv, int d, int dtype, size_t* bytes)
@@ -262,7 +267,15 @@ int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
                     size_t workspace_bytes, hipStream_t stream)
 {
     return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
-                    workspace_bytes, stream);
+                    workspace_bytes, false, stream);
+}
+
+int dit_attn_fwd_acc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Sq, int Skv, int d, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream)
+{
+    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
+                    workspace_bytes, true, stream);
 }
 
 int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, int n_parts,

@@ -167,6 +167,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// The two bf16 values of a packed pair (low half first), widened exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t w)
+{
+    return __builtin_bit_cast(float, w << 16);
+}
+
+__device__ __forceinline__ float bf16_hi(uint32_t w)
+{
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// Log-sum-exp merge of one row's new result (LSE lse_new, O_new = c_new * acc)
+// into a running one (LSE lse_old, O_old): on return O = c_new * acc +
+// c_old * O_old and LSE = lse_out, where w = exp(LSE - max) weights each side
+// ("xDiT 项目概述" sec. 3.2: the ring combines the partial results of the key
+// blocks).  A running LSE of -inf (no keys yet) leaves c_new, c_old = 0 and
+// lse_out as they are, so O_old is then never read.
+__device__ __forceinline__ void merge_weights(float lse_old, float lse_new, float& c_new,
+                                              float& c_old, float& lse_out)
+{
+    if (!(lse_old > -INFINITY))
+        return;
+    const float mx = fmaxf(lse_old, lse_new);
+    const float w_old = exp2_fast((lse_old - mx) * kLog2e);
+    const float w_new = exp2_fast((lse_new - mx) * kLog2e);
+    const float inv = 1.f / (w_old + w_new);  // one of the two weights is 1
+    c_new *= w_new * inv;
+    c_old = w_old * inv;
+    lse_out = mx + log2_fast(w_old + w_new) * kLn2;
+}
+
 // Launch through hipLaunchKernel so the launch's own status is returned
 // (hipGetLastError would also report errors left by unrelated earlier calls).
 template <typename... KArgs, typename... Args>

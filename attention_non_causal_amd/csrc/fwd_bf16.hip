@@ -586,7 +586,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int H, int Sq, int Skv, float scale_log2, int n_qtiles, int n_main, int nsplit,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse)
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int acc)
 {
     using Cfg = FwdBf16Cfg<D>;
     constexpr int kMB = Cfg::kMB;
@@ -832,17 +832,29 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
             ws_lse[(long)piece * Cfg::kBr + r] = (st.m_used + log2_fast(l_tot)) * kLn2;
     } else if (q_row < Sq) {
         uint16_t* dst = O + ((long)b * Sq * H + h) * D + (long)q_row * tok + 4 * hh;
+        float* lse_dst = LSE + ((long)b * H + h) * Sq + q_row;
+        const float lse_new = (st.m_used + log2_fast(l_tot)) * kLn2;
+        // O = c_new * acc + c_old * O_old; without a running result (acc = 0, or
+        // its LSE is -inf) that is the plain normalisation
+        float c_new = inv_l, c_old = 0.f, lse_out = lse_new;
+        if (acc)
+            merge_weights(*lse_dst, lse_new, c_new, c_old, lse_out);
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = pack_bf16x2(st.oacc[mb][4 * g + 0] * inv_l, st.oacc[mb][4 * g + 1] * inv_l);
-                w[1] = pack_bf16x2(st.oacc[mb][4 * g + 2] * inv_l, st.oacc[mb][4 * g + 3] * inv_l);
-                *reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g) = w;
+                f32x4 o = {st.oacc[mb][4 * g + 0] * c_new, st.oacc[mb][4 * g + 1] * c_new,
+                           st.oacc[mb][4 * g + 2] * c_new, st.oacc[mb][4 * g + 3] * c_new};
+                u32x2* p = reinterpret_cast<u32x2*>(dst + 32 * mb + 8 * g);
+                if (c_old != 0.f) {
+                    const u32x2 old = *p;
+                    o += c_old * f32x4{bf16_lo(old[0]), bf16_hi(old[0]), bf16_lo(old[1]),
+                                       bf16_hi(old[1])};
+                }
+                *p = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
             }
         if (hh == 0)
-            LSE[((long)b * H + h) * Sq + q_row] = (st.m_used + log2_fast(l_tot)) * kLn2;
+            *lse_dst = lse_out;
     }
 }
 
@@ -871,7 +883,7 @@ hipError_t launch_fwd_bf16_d(const FwdArgs& a, const FwdSplit& sp, hipStream_t s
     hipError_t e = launch_kernel(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(Cfg::kThreads),
                                  stream, a.q, a.k, a.v, a.o, a.lse, a.H, a.Sq, a.Skv, scale_log2,
                                  n_qtiles, split ? sp.n_main : (int)n_blocks,
-                                 split ? sp.nsplit : 1, ws_o, ws_lse);
+                                 split ? sp.nsplit : 1, ws_o, ws_lse, a.acc);
     if (e != hipSuccess || !split)
         return e;
     return launch_split_merge(a, sp, Cfg::kBr, n_qtiles, ws_o, ws_lse, nullptr, stream);

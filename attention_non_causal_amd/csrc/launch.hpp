@@ -18,6 +18,7 @@ struct FwdArgs {
     int B, H, Sq, Skv, d;
     float scale;
     void* ws;              // workspace of the split launch (see FwdSplit)
+    int acc;               // 1: merge into the running (O, LSE) held in o, lse (bf16 only)
 };
 
 // Split plan of a forward launch (split.hip): the first n_main query tiles run

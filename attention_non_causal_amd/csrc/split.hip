@@ -22,12 +22,15 @@ namespace {
 //     O = sum_p w_p O_p / sum_p w_p with w_p = exp(W_p - max_p W_p), where W_p
 //     is LSE_p, or the piece's own log-weight ws_w (if given) when O_p was
 //     normalised by a different sum than the one LSE_p is the log of.
-// One thread per (split tile, row, 4 channels).
+// With acc, the result is then merged into the running (O, LSE) the output
+// holds (merge_weights).  One thread per (split tile, row, 4 channels); the
+// threads of one row sit in one wave, so every read of the row's LSE comes
+// before its write.
 template <int D>
 __global__ __launch_bounds__(256) void split_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const float* __restrict__ ws_w, uint16_t* __restrict__ O, float* __restrict__ LSE, int H,
-    int Sq, int rows, int n_qtiles, int n_main, int nsplit, int n_tail)
+    int Sq, int rows, int n_qtiles, int n_main, int nsplit, int n_tail, int acc)
 {
     constexpr int kChunks = D / 4;
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -52,21 +55,28 @@ __global__ __launch_bounds__(256) void split_merge_kernel(
         mw = fmaxf(mw, wo[(p0 + p) * rows + r]);
     }
     float lsum = 0.f, wsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sum_o = {0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < nsplit; ++p) {
         lsum += exp2_fast((ws_lse[(p0 + p) * rows + r] - m) * kLog2e);
         const float w = exp2_fast((wo[(p0 + p) * rows + r] - mw) * kLog2e);
         const f32x4 o = *reinterpret_cast<const f32x4*>(ws_o + ((p0 + p) * rows + r) * D + 4 * c);
-        acc += w * o;
+        sum_o += w * o;
         wsum += w;
     }
-    const float inv = 1.f / wsum;
-    u32x2 out;
-    out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(O + (((long)b * Sq + q_row) * H + h) * D + 4 * c) = out;
+    float* lse_dst = LSE + ((long)b * H + h) * Sq + q_row;
+    const float lse_new = m + log2_fast(lsum) * kLn2;
+    float c_new = 1.f / wsum, c_old = 0.f, lse_out = lse_new;
+    if (acc)
+        merge_weights(*lse_dst, lse_new, c_new, c_old, lse_out);
+    u32x2* dst = reinterpret_cast<u32x2*>(O + (((long)b * Sq + q_row) * H + h) * D + 4 * c);
+    f32x4 o = c_new * sum_o;
+    if (c_old != 0.f) {
+        const u32x2 old = *dst;
+        o += c_old * f32x4{bf16_lo(old[0]), bf16_hi(old[0]), bf16_lo(old[1]), bf16_hi(old[1])};
+    }
+    *dst = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     if (c == 0)
-        LSE[((long)b * H + h) * Sq + q_row] = m + log2_fast(lsum) * kLn2;
+        *lse_dst = lse_out;
 }
 
 }  // namespace
@@ -103,9 +113,11 @@ hipError_t launch_split_merge(const FwdArgs& a, const FwdSplit& sp, int rows, in
     auto* o = static_cast<uint16_t*>(a.o);
     if (a.d == 64)
         return launch_kernel(split_merge_kernel<64>, grid, block, stream, ws_o, ws_lse, ws_w, o,
-                             a.lse, a.H, a.Sq, rows, n_qtiles, sp.n_main, sp.nsplit, sp.n_tail);
+                             a.lse, a.H, a.Sq, rows, n_qtiles, sp.n_main, sp.nsplit, sp.n_tail,
+                             a.acc);
     return launch_kernel(split_merge_kernel<128>, grid, block, stream, ws_o, ws_lse, ws_w, o,
-                         a.lse, a.H, a.Sq, rows, n_qtiles, sp.n_main, sp.nsplit, sp.n_tail);
+                         a.lse, a.H, a.Sq, rows, n_qtiles, sp.n_main, sp.nsplit, sp.n_tail,
+                         a.acc);
 }
 
 }  // namespace dit

@@ -119,6 +119,66 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
     return out, lse
 
 
+def attention_acc(q, k, v, out, lse, scale: float | None = None, stream=None,
+                  workspace="auto"):
+    """Merge bf16 attention over the keys k/v into the running result (out,
+    lse) over earlier keys (dit_attn_fwd_acc): rows whose lse is -inf have no
+    keys yet.  k, v: tensors, or (pointer, Skv) pairs for blocks of a larger
+    tensor (B must then be 1).  workspace as for attention."""
+    import torch
+    _require(q, torch.bfloat16, "q")
+    B, Sq, H, d = q.shape
+    if isinstance(k, tuple):
+        (k, Skv), (v, _) = k, v
+    else:
+        for t, n in ((k, "k"), (v, "v")):
+            _require(t, torch.bfloat16, n)
+        Skv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d, _lib.DIT_DTYPE_BF16)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.dit_attn_fwd_acc(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                          workspace, n_bytes, stream)
+    return out, lse
+
+
+def ring_share_attention_acc(q, k, v, n_chunks: int, scale: float | None = None, out=None,
+                             lse=None, workspace="auto", stream=None):
+    """One ring rank's share as a ring loop runs it: the running result starts
+    empty (lse = -inf) and each of ``n_chunks`` consecutive KV chunks is merged
+    into it as it is processed (dit_attn_fwd_acc on pointer offsets into k/v,
+    so B must be 1) -- no partial outputs, no separate merge."""
+    import torch
+    B, Sq, H, d = q.shape
+    Skv = k.shape[1]
+    if B != 1:
+        raise ValueError("KV chunks are pointer offsets: B must be 1")
+    if Skv % n_chunks:
+        raise ValueError("Skv must be a multiple of n_chunks")
+    c = Skv // n_chunks
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, c, d, _lib.DIT_DTYPE_BF16)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    lse.fill_(-math.inf)
+    es = k.element_size()
+    for i in range(n_chunks):
+        off = i * c * H * d * es
+        attention_acc(q, (k.data_ptr() + off, c), (v.data_ptr() + off, c), out, lse, scale,
+                      stream, workspace)
+    return out, lse
+
+
 def ring_share_attention(q, k, v, n_chunks: int, scale: float | None = None, parts=None,
                          out=None, lse=None, stream=None):
     """One ring rank's share of ring attention, run locally: the local queries

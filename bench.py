@@ -262,11 +262,22 @@ def run_extras(dev, steps, warmup):
     mms = time_batched(lambda: F.merge(parts[0], parts[1], out=o, lse=lse), 4 * steps, warmup)
     merge_bytes = W.n_chunks * (W.Sq * W.H * W.d * 2 + W.H * W.Sq * 4) + W.Sq * W.H * W.d * 2 \
         + W.H * W.Sq * 4
+    # the same share as a ring loop runs it: each chunk merged into the running
+    # result by dit_attn_fwd_acc (no partial outputs, no separate merge)
+    nws = _lib.dit_attn_fwd_workspace_size(1, W.H, W.Sq, W.chunk, W.d)
+    aws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    _, aevs = time_launches(
+        lambda: F.ring_share_attention_acc(q, k, v, W.n_chunks, W.scale, out=o, lse=lse,
+                                           workspace=aws),
+        steps, warmup)
+    ams = float(np.mean(aevs))
     res["wan_ring"] = {"total_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1),
                        "merge_ms": round(mms, 4),
-                       "merge_GBs": round(merge_bytes / mms / 1e6, 1)}
+                       "merge_GBs": round(merge_bytes / mms / 1e6, 1),
+                       "acc_total_ms": round(ams, 4), "acc_tflops": round(W.flops / ams / 1e9, 1)}
     log(f"extra wan_ring: {ms:.3f} ms total ({res['wan_ring']['tflops']} TFLOP/s), merge "
-        f"{mms:.3f} ms = {res['wan_ring']['merge_GBs']} GB/s")
+        f"{mms:.3f} ms = {res['wan_ring']['merge_GBs']} GB/s; merged as it runs "
+        f"(dit_attn_fwd_acc) {ams:.3f} ms ({res['wan_ring']['acc_tflops']} TFLOP/s)")
     del q, k, v, parts, o, lse
 
     # fp8: the FLUX-like shape with 1% x8 outlier channels, quantised per

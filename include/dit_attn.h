@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DIT_ATTN_VERSION 10200 /* major*10000 + minor*100 + patch */
+#define DIT_ATTN_VERSION 10300 /* major*10000 + minor*100 + patch */
 
 enum dit_status {
     DIT_OK = 0,
@@ -62,7 +62,7 @@ enum dit_status {
     DIT_ERR_VALUE = 5,       /* scale not finite or not > 0                        */
     DIT_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap     */
     DIT_ERR_HIP = 7,         /* the HIP launch (or device query) reported an error */
-    DIT_ERR_WORKSPACE = 8    /* dit_attn_fwd_ws: workspace NULL, smaller than
+    DIT_ERR_WORKSPACE = 8    /* dit_attn_fwd_ws/_acc: workspace NULL, smaller than
                                 dit_attn_fwd_workspace_size, not 16-byte aligned,
                                 or overlapping a tensor                            */
 };
@@ -138,6 +138,30 @@ int dit_attn_fwd_workspace_size(int B, int H, int Sq, int Skv, int d, int dtype,
 int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Sq, int Skv, int d, float scale, int dtype,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dit_attn_fwd_acc -- the bf16 forward pass over one block of keys, merged
+ * into a running result over the key blocks before it: what a rank of ring
+ * attention runs each time a KV block arrives ("xDiT 项目概述" sec. 3.2: the
+ * ring dimension splits the sequence into blocks passed around the GPUs, and
+ * each GPU combines the partial results), without writing partial outputs or
+ * running a separate merge.
+ *
+ *   Arguments as dit_attn_fwd_ws (workspace rules included: the split launch
+ *   is used when dit_attn_fwd_workspace_size is not 0), except:
+ *   dtype: DIT_DTYPE_BF16 only (fp8: DIT_ERR_UNSUPPORTED).
+ *   o, lse: on entry the running result (bf16 O, fp32 natural-log LSE) over
+ *       the earlier key blocks -- a row whose LSE is -inf has no keys yet and
+ *       its O is not read (so a first block needs only LSE set to -inf); on
+ *       return the result over those keys and this block's, computed as
+ *       dit_attn_merge would merge the two, except that this block's O enters
+ *       in fp32 (it is never rounded to bf16 on its own).  Any other LSE value
+ *       on entry (NaN, +inf) is not supported.
+ *   Errors as dit_attn_fwd_ws.
+ */
+int dit_attn_fwd_acc(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Sq, int Skv, int d, float scale, int dtype,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dit_attn_merge -- combine n partial attention results over disjoint key

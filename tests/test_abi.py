@@ -25,8 +25,8 @@ def fwd(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
 def test_library_exports_header_functions():
     names = _lib.header_functions()
     assert set(names) == {"dit_attn_fwd", "dit_attn_fwd_workspace_size", "dit_attn_fwd_ws",
-                          "dit_attn_merge", "dit_quant_fp8", "dit_status_string",
-                          "dit_version"}
+                          "dit_attn_fwd_acc", "dit_attn_merge", "dit_quant_fp8",
+                          "dit_status_string", "dit_version"}
     lib = _lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +37,7 @@ def test_library_exports_header_functions():
 
 
 def test_version_and_status_strings():
-    assert _lib.dit_version() == 10200
+    assert _lib.dit_version() == 10300
     texts = [_lib.dit_status_string(s) for s in range(9)]
     assert len(set(texts)) == 9 and all(texts)
     assert _lib.dit_status_string(99) == "unknown status"
@@ -164,6 +164,31 @@ def test_fwd_ws_rejects_like_fwd(kw, status):
     dit_attn_fwd does, before any HIP call."""
     assert fwd_ws(**kw) == status
     assert fwd(**kw) == status
+
+
+def fwd_acc(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
+            dtype=DIT_DTYPE_BF16, ws=None, ws_bytes=0):
+    return _lib.dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, ws,
+                                        ws_bytes, stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), DIT_ERR_NULL), (dict(lse=None), DIT_ERR_NULL),
+    (dict(dtype=2), DIT_ERR_UNSUPPORTED), (dict(d=96), DIT_ERR_UNSUPPORTED),
+    (dict(B=0), DIT_ERR_SHAPE), (dict(H=64, Skv=1 << 18, d=128), DIT_ERR_SHAPE),
+    (dict(scale=math.nan), DIT_ERR_VALUE), (dict(o=O + 8), DIT_ERR_ALIGN),
+    (dict(o=Q), DIT_ERR_ALIAS), (dict(lse=V), DIT_ERR_ALIAS),
+])
+def test_fwd_acc_rejects_like_fwd(kw, status):
+    """The accumulating entry point validates its arguments as dit_attn_fwd
+    does, before any HIP call."""
+    assert fwd_acc(**kw) == status
+
+
+def test_fwd_acc_is_bf16_only():
+    """The merge into a running result exists for the bf16 path only; the fp8
+    dtype is refused before its descriptors are even read."""
+    assert fwd_acc(dtype=DIT_DTYPE_FP8_E4M3) == DIT_ERR_UNSUPPORTED
 
 
 def test_workspace_size_argument_checks():

@@ -1,0 +1,143 @@
+"""GPU tests of dit_attn_fwd_acc (the bf16 forward pass over one block of keys
+merged into a running result), through the C ABI, against the fp64 oracle
+run on all the keys at once.
+
+Gates as for dit_attn_fwd: max|dO| <= 1e-2, max|dLSE| <= 1e-3, relative RMS
+<= 1e-2.  Where few keys make |O| as large as |V| the O budget is the bound of
+the arithmetic: each block's weights rounded to bf16 before P.V (<= 2^-9
+relative) and the running O rounded to bf16 after each of the n blocks
+(<= 2^-9 |O| each), so |dO| <= (n + 1) 2^-9 max|V|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_non_causal_amd import _lib, functional as F, workloads as wl
+from tests import _gpu
+from tests._gpu import compare, dev_bf16, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(B, H, Sq, Skv, d, seed):
+    g = wl.generate("tiny", seed=seed, B=B, H=H, Sq=Sq, Skv=Skv, d=d)
+    return g["q"], g["k"], g["v"]
+
+
+def _o_tol(v_bits, n_blocks):
+    vmax = float(np.abs((np.asarray(v_bits, dtype=np.uint16).astype(np.uint32) << 16)
+                        .view(np.float32)).max())
+    return max(_gpu.BF16_O_TOL, (n_blocks + 1) * 2.0 ** -9 * vmax)
+
+
+def _acc_blocks(qd, kd, vd, bounds, scale, o, lse):
+    """Merge attention over key blocks [bounds[i], bounds[i+1]) into (o, lse)."""
+    B, Sq, H, d = qd.shape
+    es = kd.element_size()
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        off = a * H * d * es
+        F.attention_acc(qd, (kd.data_ptr() + off, b - a), (vd.data_ptr() + off, b - a), o, lse,
+                        scale)
+
+
+@pytest.mark.parametrize("Sq,bounds,d", [
+    (300, [0, 300, 700, 1000], 64),      # uneven blocks with ragged tails
+    (129, [0, 64, 1000], 128),           # one block of a single key tile
+    (256, [0, 1, 2, 700], 128),          # blocks of one key
+    (70, [0, 4000, 8000], 128),          # two long blocks (split launches)
+])
+def test_acc_blocks_equal_attention_over_all_keys(Sq, bounds, d):
+    B, H, Skv = 1, 2, bounds[-1]
+    say(f"fwd_acc blocks {bounds} Sq{Sq} d{d}")
+    q, k, v = _draw(B, H, Sq, Skv, d, seed=5000 + Sq + Skv + d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o = torch.full((B, Sq, H, d), float("nan"), dtype=torch.bfloat16, device=qd.device)
+    lse = torch.full((B, H, Sq), -math.inf, dtype=torch.float32, device=qd.device)
+    _acc_blocks(qd, kd, vd, bounds, scale, o, lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale)
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, o_tol=_o_tol(v, len(bounds) - 1),
+            what=f"acc blocks {bounds} d{d}")
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,d", [(2, 3, 300, 333, 64), (1, 2, 256, 2048, 128)])
+def test_acc_into_empty_result_is_the_plain_forward(B, H, Sq, Skv, d):
+    """With no running result (LSE -inf; its O, here NaN, is never read) the
+    call writes exactly what dit_attn_fwd_ws writes (the second shape is split
+    over the keys on any GPU with >= 8 CUs, so the merge kernel's path is
+    covered too)."""
+    say(f"fwd_acc into an empty result B{B} H{H} Sq{Sq} Skv{Skv} d{d}")
+    q, k, v = _draw(B, H, Sq, Skv, d, seed=5100 + Skv)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    scale = 0.09
+    n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=qd.device)
+    o_ref = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=qd.device)
+    l_ref = torch.empty((B, H, Sq), dtype=torch.float32, device=qd.device)
+    _lib.dit_attn_fwd_ws(qd, kd, vd, o_ref, l_ref, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                         ws, n)
+    o = torch.full_like(o_ref, float("nan"))
+    lse = torch.full_like(l_ref, -math.inf)
+    _lib.dit_attn_fwd_acc(qd, kd, vd, o, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16, ws, n)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(lse, l_ref)
+
+
+def test_acc_equals_merge_of_two_forwards():
+    """Merging a block into a result is the two-part dit_attn_merge, except
+    that the block's own O is not rounded to bf16 first: before their final
+    rounding the two differ by at most that rounding (2^-9 |O_2|, times a
+    weight <= 1), and each final rounding moves a value by at most half an ulp
+    -- together one ulp, <= 2^-7 |O| for bf16."""
+    B, H, Sq, Skv, d = 1, 3, 200, 900, 128
+    say("fwd_acc vs fwd + merge")
+    q, k, v = _draw(B, H, Sq, Skv, d, seed=5200)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    scale = 0.088
+    half = 500
+    o1, l1 = F.attention(qd, kd[:, :half].contiguous(), vd[:, :half].contiguous(), scale)
+    o2, l2 = F.attention(qd, kd[:, half:].contiguous(), vd[:, half:].contiguous(), scale)
+    om, lm = F.merge([o1, o2], [l1, l2])
+    oa, la = o1.clone(), l1.clone()
+    F.attention_acc(qd, kd[:, half:].contiguous(), vd[:, half:].contiguous(), oa, la, scale)
+    torch.cuda.synchronize()
+    d_o = np.abs(host_f64(oa) - host_f64(om))
+    bound = 2.0 ** -9 * np.abs(host_f64(o2)) + 2.0 ** -7 * np.abs(host_f64(om)) + 1e-6
+    assert (d_o <= bound).all(), f"max excess {(d_o - bound).max():.3e}"
+    assert np.abs(host_f64(la) - host_f64(lm)).max() <= 1e-5
+
+
+def test_acc_errors():
+    B, H, Sq, Skv, d = 1, 2, 256, 2048, 128
+    q, k, v = _draw(B, H, Sq, Skv, d, seed=5300)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=qd.device)
+    lse = torch.full((B, H, Sq), -math.inf, dtype=torch.float32, device=qd.device)
+    n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d)
+    assert n > 0, "this shape is expected to be split"
+    st = _lib.dit_attn_fwd_acc_status(qd, kd, vd, o, lse, B, H, Sq, Skv, d, 0.1,
+                                      _lib.DIT_DTYPE_BF16, None, 0)
+    assert st == _lib.DIT_ERR_WORKSPACE
+    torch.cuda.synchronize()
+
+
+def test_wan_ring_share_accumulated_full_size():
+    """The Wan-like ring share as a ring loop runs it: 4 KV chunks merged into
+    the running result one after another (no partial outputs, no separate
+    merge), against the oracle over all 32760 keys on sampled rows."""
+    W = wl.WORKLOADS["wan_ring"]
+    say("wan ring share (accumulated): generating inputs")
+    g = wl.generate("wan_ring")
+    q, k, v = dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"])
+    say("wan ring share (accumulated): 4 chunk forwards merged as they run")
+    o, l = F.ring_share_attention_acc(q, k, v, W.n_chunks, W.scale)
+    torch.cuda.synchronize()
+    rows = wl.sample_rows(W.Sq, 16)
+    say("wan ring share (accumulated): oracle on sampled rows")
+    o_ref, l_ref = oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
+    compare(host_f64(o)[:, rows], host_f64(l)[:, :, rows], o_ref, l_ref, what="wan_ring_acc")
