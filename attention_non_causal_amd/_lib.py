@@ -66,7 +66,8 @@ def load():
     lib.dit_attn_fwd_workspace_size.restype = I
     lib.dit_attn_fwd_ws.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
     lib.dit_attn_fwd_ws.restype = I
-    lib.dit_attn_fwd_acc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
+    lib.dit_attn_fwd_acc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, ctypes.c_longlong, P,
+                                     ctypes.c_size_t, P]
     lib.dit_attn_fwd_acc.restype = I
     lib.dit_attn_merge.argtypes = [P, P, I, P, P, I, I, I, I, P]
     lib.dit_attn_merge.restype = I
@@ -181,20 +182,22 @@ def dit_attn_fwd_ws(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF
 
 
 def dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,
-                            workspace=None, workspace_bytes=0, stream=None) -> int:
+                            kv_batch_tokens=0, workspace=None, workspace_bytes=0,
+                            stream=None) -> int:
     """Call dit_attn_fwd_acc and return its status code (no exception)."""
     args = [_fwd_operand(t, dtype) for t in (q, k, v)]
     return load().dit_attn_fwd_acc(args[0], args[1], args[2], _addr(o), _addr(lse), int(B),
                                    int(H), int(Sq), int(Skv), int(d), float(scale), int(dtype),
-                                   _addr(workspace), int(workspace_bytes), _stream(stream))
+                                   int(kv_batch_tokens), _addr(workspace), int(workspace_bytes),
+                                   _stream(stream))
 
 
 def dit_attn_fwd_acc(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,
-                     workspace=None, workspace_bytes=0, stream=None) -> None:
+                     kv_batch_tokens=0, workspace=None, workspace_bytes=0, stream=None) -> None:
     """The bf16 forward pass over one key block merged into the running
     (o, lse) (see the header)."""
-    _check(dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, workspace,
-                                   workspace_bytes, stream))
+    _check(dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype,
+                                   kv_batch_tokens, workspace, workspace_bytes, stream))
 
 
 def dit_attn_merge_status(o_parts, lse_parts, n_parts, o, lse, B, H, Sq, d, stream=None) -> int:

@@ -122,10 +122,11 @@ int check_fwd_shape(int B, int H, int Sq, int Skv, int d, int dtype)
 }
 
 // dit_attn_fwd, dit_attn_fwd_ws and dit_attn_fwd_acc; with_ws selects the
-// split launch, acc the merge into the running result held in o, lse.
+// split launch, acc the merge into the running result held in o, lse, and
+// kv_batch_tokens (acc only; 0: Skv) the distance between batches of k, v.
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int Sq, int Skv, int d, float scale, int dtype, bool with_ws, void* ws,
-             size_t ws_bytes, bool acc, hipStream_t stream)
+             size_t ws_bytes, bool acc, long long kv_batch_tokens, hipStream_t stream)
 {
     if (!q || !k || !v || !o || !lse)
         return DIT_ERR_NULL;
@@ -146,6 +147,15 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
         return DIT_ERR_SHAPE;
     // K and V of one batch are addressed with 32-bit buffer offsets
     if (kv_bytes / B > kMaxKvBytesPerBatch)
+        return DIT_ERR_SHAPE;
+    // batches of K and V kv_batch_tokens apart: they span (B-1) * that + Skv tokens
+    if (kv_batch_tokens < 0 || (kv_batch_tokens > 0 && kv_batch_tokens < Skv) ||
+        kv_batch_tokens > 0x7fffffffLL)
+        return DIT_ERR_SHAPE;
+    const int64_t kv_span = kv_batch_tokens == 0
+                                ? kv_bytes
+                                : checked_bytes({(int64_t)(B - 1) * kv_batch_tokens + Skv, H, d, esz});
+    if (kv_span < 0)
         return DIT_ERR_SHAPE;
     if (!(isfinite(scale) && scale > 0.f))
         return DIT_ERR_VALUE;
@@ -174,7 +184,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
         return DIT_ERR_ALIGN;
 
     const Range ro = range(o, o_bytes), rl = range(lse, lse_bytes);
-    const Range inputs[] = {range(a.q, q_bytes), range(a.k, kv_bytes), range(a.v, kv_bytes)};
+    const Range inputs[] = {range(a.q, q_bytes), range(a.k, kv_span), range(a.v, kv_span)};
     for (const Range& in : inputs)
         if (overlap(ro, in) || overlap(rl, in))
             return DIT_ERR_ALIAS;
@@ -200,6 +210,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.d = d;
     a.scale = scale;
     a.acc = acc ? 1 : 0;
+    a.kv_batch_tokens = (long)kv_batch_tokens;
 
     dit::FwdSplit split = {};
     if (with_ws) {
@@ -241,7 +252,7 @@ extern "C" {
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int Sq, int Skv, int d, float scale, int dtype, hipStream_t stream)
 {
-    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, false, nullptr, 0, false,
+    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, false, nullptr, 0, false, 0,
                     stream);
 }
 
@@ -267,15 +278,16 @@ int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
                     size_t workspace_bytes, hipStream_t stream)
 {
     return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
-                    workspace_bytes, false, stream);
+                    workspace_bytes, false, 0, stream);
 }
 
 int dit_attn_fwd_acc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int H, int Sq, int Skv, int d, float scale, int dtype, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream)
+                     int H, int Sq, int Skv, int d, float scale, int dtype,
+                     long long kv_batch_tokens, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream)
 {
     return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
-                    workspace_bytes, true, stream);
+                    workspace_bytes, true, kv_batch_tokens, stream);
 }
 
 int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, int n_parts,

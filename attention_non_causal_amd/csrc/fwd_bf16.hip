@@ -586,7 +586,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int H, int Sq, int Skv, float scale_log2, int n_qtiles, int n_main, int nsplit,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, int acc)
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int acc, long kv_bstride)
 {
     using Cfg = FwdBf16Cfg<D>;
     constexpr int kMB = Cfg::kMB;
@@ -647,8 +647,9 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     st.scale_log2 = scale_log2;
     st.tok_bytes = (uint32_t)(tok * 2);
     {
-        const uint16_t* Kbh = K + ((long)b * Skv * H + h) * D;
-        const uint16_t* Vbh = V + ((long)b * Skv * H + h) * D;
+        // batches of K and V lie kv_bstride tokens apart (Skv when contiguous)
+        const uint16_t* Kbh = K + ((long)b * kv_bstride * H + h) * D;
+        const uint16_t* Vbh = V + ((long)b * kv_bstride * H + h) * D;
         // Byte extent of this (b, h)'s keys: rows 0 .. Skv-1 (callers guarantee < 2^32).
         const int extent = (int)((uint32_t)(Skv - 1) * st.tok_bytes + kRow);
         st.k_rsrc = make_rsrc(Kbh, extent);
@@ -883,7 +884,8 @@ hipError_t launch_fwd_bf16_d(const FwdArgs& a, const FwdSplit& sp, hipStream_t s
     hipError_t e = launch_kernel(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(Cfg::kThreads),
                                  stream, a.q, a.k, a.v, a.o, a.lse, a.H, a.Sq, a.Skv, scale_log2,
                                  n_qtiles, split ? sp.n_main : (int)n_blocks,
-                                 split ? sp.nsplit : 1, ws_o, ws_lse, a.acc);
+                                 split ? sp.nsplit : 1, ws_o, ws_lse, a.acc,
+                                 a.kv_batch_tokens > 0 ? a.kv_batch_tokens : (long)a.Skv);
     if (e != hipSuccess || !split)
         return e;
     return launch_split_merge(a, sp, Cfg::kBr, n_qtiles, ws_o, ws_lse, nullptr, stream);

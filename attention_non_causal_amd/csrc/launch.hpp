@@ -19,6 +19,7 @@ struct FwdArgs {
     float scale;
     void* ws;              // workspace of the split launch (see FwdSplit)
     int acc;               // 1: merge into the running (O, LSE) held in o, lse (bf16 only)
+    long kv_batch_tokens;  // tokens between consecutive batches of k, v (bf16 path; 0: Skv)
 };
 
 // Split plan of a forward launch (split.hip): the first n_main query tiles run

@@ -120,11 +120,12 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
 
 
 def attention_acc(q, k, v, out, lse, scale: float | None = None, stream=None,
-                  workspace="auto"):
+                  workspace="auto", kv_batch_tokens: int = 0):
     """Merge bf16 attention over the keys k/v into the running result (out,
     lse) over earlier keys (dit_attn_fwd_acc): rows whose lse is -inf have no
-    keys yet.  k, v: tensors, or (pointer, Skv) pairs for blocks of a larger
-    tensor (B must then be 1).  workspace as for attention."""
+    keys yet.  k, v: tensors, or (pointer, Skv) pairs for a block of larger
+    tensors whose batches lie kv_batch_tokens tokens apart (0: Skv).
+    workspace as for attention."""
     import torch
     _require(q, torch.bfloat16, "q")
     B, Sq, H, d = q.shape
@@ -143,7 +144,7 @@ def attention_acc(q, k, v, out, lse, scale: float | None = None, stream=None,
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
     n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _lib.dit_attn_fwd_acc(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
-                          workspace, n_bytes, stream)
+                          kv_batch_tokens, workspace, n_bytes, stream)
     return out, lse
 
 
@@ -152,12 +153,11 @@ def ring_share_attention_acc(q, k, v, n_chunks: int, scale: float | None = None,
     """One ring rank's share as a ring loop runs it: the running result starts
     empty (lse = -inf) and each of ``n_chunks`` consecutive KV chunks is merged
     into it as it is processed (dit_attn_fwd_acc on pointer offsets into k/v,
-    so B must be 1) -- no partial outputs, no separate merge."""
+    batches Skv tokens apart, so any B) -- no partial outputs, no separate
+    merge."""
     import torch
     B, Sq, H, d = q.shape
     Skv = k.shape[1]
-    if B != 1:
-        raise ValueError("KV chunks are pointer offsets: B must be 1")
     if Skv % n_chunks:
         raise ValueError("Skv must be a multiple of n_chunks")
     c = Skv // n_chunks
@@ -175,7 +175,7 @@ def ring_share_attention_acc(q, k, v, n_chunks: int, scale: float | None = None,
     for i in range(n_chunks):
         off = i * c * H * d * es
         attention_acc(q, (k.data_ptr() + off, c), (v.data_ptr() + off, c), out, lse, scale,
-                      stream, workspace)
+                      stream, workspace, kv_batch_tokens=Skv)
     return out, lse
 
 

@@ -150,6 +150,11 @@ int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
  *   Arguments as dit_attn_fwd_ws (workspace rules included: the split launch
  *   is used when dit_attn_fwd_workspace_size is not 0), except:
  *   dtype: DIT_DTYPE_BF16 only (fp8: DIT_ERR_UNSUPPORTED).
+ *   kv_batch_tokens: tokens between the starts of consecutive batches in k
+ *       and v (0: Skv, contiguous).  With B > 1 the key block is usually a
+ *       slice [s0, s0 + Skv) of larger [B][S][H][d] tensors: pass k, v offset
+ *       by s0 tokens and kv_batch_tokens = S.  Must be 0 or >= Skv (else
+ *       DIT_ERR_SHAPE); the batches' extents are checked for aliasing.
  *   o, lse: on entry the running result (bf16 O, fp32 natural-log LSE) over
  *       the earlier key blocks -- a row whose LSE is -inf has no keys yet and
  *       its O is not read (so a first block needs only LSE set to -inf); on
@@ -161,7 +166,8 @@ int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
  */
 int dit_attn_fwd_acc(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int Sq, int Skv, int d, float scale, int dtype,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+                     long long kv_batch_tokens, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /*
  * dit_attn_merge -- combine n partial attention results over disjoint key

@@ -167,9 +167,10 @@ def test_fwd_ws_rejects_like_fwd(kw, status):
 
 
 def fwd_acc(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
-            dtype=DIT_DTYPE_BF16, ws=None, ws_bytes=0):
-    return _lib.dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, ws,
-                                        ws_bytes, stream=0)
+            dtype=DIT_DTYPE_BF16, kv_batch_tokens=0, ws=None, ws_bytes=0):
+    return _lib.dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype,
+                                        kv_batch_tokens=kv_batch_tokens, workspace=ws,
+                                        workspace_bytes=ws_bytes, stream=0)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -183,6 +184,18 @@ def test_fwd_acc_rejects_like_fwd(kw, status):
     """The accumulating entry point validates its arguments as dit_attn_fwd
     does, before any HIP call."""
     assert fwd_acc(**kw) == status
+
+
+def test_fwd_acc_kv_batch_stride_checks():
+    """kv_batch_tokens: 0 (contiguous) or at least Skv; the batches it spreads
+    K and V over are part of their extent for the aliasing checks."""
+    for kbt in (-1, 255, 1 << 31):
+        assert fwd_acc(kv_batch_tokens=kbt) == DIT_ERR_SHAPE
+    # B2 H2 d64: K spans (1000 + 256) tokens x 256 bytes; an output placed 600
+    # tokens into it overlaps the second batch's keys (but not a contiguous K)
+    o_in_k = K + 600 * 2 * 64 * 2
+    assert fwd_acc(B=2, o=o_in_k, kv_batch_tokens=1000) == DIT_ERR_ALIAS
+    assert fwd_acc(B=2, o=o_in_k) != DIT_ERR_ALIAS
 
 
 def test_fwd_acc_is_bf16_only():

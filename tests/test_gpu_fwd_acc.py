@@ -34,23 +34,27 @@ def _o_tol(v_bits, n_blocks):
 
 
 def _acc_blocks(qd, kd, vd, bounds, scale, o, lse):
-    """Merge attention over key blocks [bounds[i], bounds[i+1]) into (o, lse)."""
+    """Merge attention over key blocks [bounds[i], bounds[i+1]) into (o, lse):
+    each block is a pointer offset into k/v, whose batches lie Skv tokens apart."""
     B, Sq, H, d = qd.shape
+    Skv = kd.shape[1]
     es = kd.element_size()
     for a, b in zip(bounds[:-1], bounds[1:]):
         off = a * H * d * es
         F.attention_acc(qd, (kd.data_ptr() + off, b - a), (vd.data_ptr() + off, b - a), o, lse,
-                        scale)
+                        scale, kv_batch_tokens=Skv)
 
 
-@pytest.mark.parametrize("Sq,bounds,d", [
-    (300, [0, 300, 700, 1000], 64),      # uneven blocks with ragged tails
-    (129, [0, 64, 1000], 128),           # one block of a single key tile
-    (256, [0, 1, 2, 700], 128),          # blocks of one key
-    (70, [0, 4000, 8000], 128),          # two long blocks (split launches)
+@pytest.mark.parametrize("B,Sq,bounds,d", [
+    (1, 300, [0, 300, 700, 1000], 64),   # uneven blocks with ragged tails
+    (1, 129, [0, 64, 1000], 128),        # one block of a single key tile
+    (1, 256, [0, 1, 2, 700], 128),       # blocks of one key
+    (1, 70, [0, 4000, 8000], 128),       # two long blocks (split launches)
+    (2, 100, [0, 300, 700, 1000], 128),  # batches: blocks are strided slices
+    (3, 77, [0, 129, 500], 64),
 ])
-def test_acc_blocks_equal_attention_over_all_keys(Sq, bounds, d):
-    B, H, Skv = 1, 2, bounds[-1]
+def test_acc_blocks_equal_attention_over_all_keys(B, Sq, bounds, d):
+    H, Skv = 2, bounds[-1]
     say(f"fwd_acc blocks {bounds} Sq{Sq} d{d}")
     q, k, v = _draw(B, H, Sq, Skv, d, seed=5000 + Sq + Skv + d)
     scale = float(np.float32(1 / math.sqrt(d)))
@@ -82,7 +86,8 @@ def test_acc_into_empty_result_is_the_plain_forward(B, H, Sq, Skv, d):
                          ws, n)
     o = torch.full_like(o_ref, float("nan"))
     lse = torch.full_like(l_ref, -math.inf)
-    _lib.dit_attn_fwd_acc(qd, kd, vd, o, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16, ws, n)
+    _lib.dit_attn_fwd_acc(qd, kd, vd, o, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                          workspace=ws, workspace_bytes=n)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
     assert torch.equal(lse, l_ref)
@@ -121,7 +126,7 @@ def test_acc_errors():
     n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d)
     assert n > 0, "this shape is expected to be split"
     st = _lib.dit_attn_fwd_acc_status(qd, kd, vd, o, lse, B, H, Sq, Skv, d, 0.1,
-                                      _lib.DIT_DTYPE_BF16, None, 0)
+                                      _lib.DIT_DTYPE_BF16)
     assert st == _lib.DIT_ERR_WORKSPACE
     torch.cuda.synchronize()
 
