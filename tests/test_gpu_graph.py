@@ -1,0 +1,115 @@
+"""The library's calls captured into a HIP graph (through torch.cuda.CUDAGraph,
+which captures the stream the calls launch on): the header promises that every
+call only enqueues work, allocates nothing and never synchronises.
+
+The graph holds the split bf16 forward (forward kernel + split merge), a
+two-part merge, the fp8 quantiser with the fp8 split forward, and a chain of
+two dit_attn_fwd_acc blocks whose running LSE is reset by a copy (no memset is
+recorded).  It is replayed several times with the program's own eager work
+and synchronisations in between; every replay must reproduce the eager results
+bit for bit (the kernels are deterministic).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from attention_non_causal_amd import _lib, functional as F, workloads as wl
+from tests._gpu import dev_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, Sq, Skv, d, seed):
+    g = wl.generate("tiny", seed=seed, B=B, H=H, Sq=Sq, Skv=Skv, d=d)
+    return dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"])
+
+
+def test_graph_replays_match_eager():
+    B, H, Sq, Skv, d = 1, 2, 256, 2048, 128
+    say("graph capture: inputs and eager results")
+    q, k, v = _inputs(B, H, Sq, Skv, d, seed=6000)
+    scale = 0.088
+    dev = q.device
+    ws = F.workspace_for(q, k)
+    assert ws is not None, "this shape is expected to be split"
+    half = Skv // 2
+    k1, v1 = k[:, :half].contiguous(), v[:, :half].contiguous()
+    k2, v2 = k[:, half:].contiguous(), v[:, half:].contiguous()
+    nws_half = _lib.dit_attn_fwd_workspace_size(B, H, Sq, half, d)
+    ws_half = torch.empty(max(nws_half, 16), dtype=torch.uint8, device=dev)
+    neg_inf = torch.full((B, H, Sq), -math.inf, dtype=torch.float32, device=dev)
+    nblk = (Skv + 127) // 128
+
+    def bufs():
+        return dict(
+            o=torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=dev),
+            l=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+            o1=torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=dev),
+            l1=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+            o2=torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=dev),
+            l2=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+            om=torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=dev),
+            lm=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+            q8=torch.empty((B, Sq, H, d), dtype=torch.uint8, device=dev),
+            qs=torch.empty((B, H, (Sq + 127) // 128), dtype=torch.float32, device=dev),
+            k8=torch.empty((B, Skv, H, d), dtype=torch.uint8, device=dev),
+            ks=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+            v8=torch.empty((B, Skv, H, d), dtype=torch.uint8, device=dev),
+            vs=torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+            of=torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=dev),
+            lf=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+            oa=torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=dev),
+            la=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+        )
+
+    ws8 = None
+
+    def work(t):
+        nonlocal ws8
+        F.attention(q, k, v, scale, out=t["o"], lse=t["l"], workspace=ws)
+        F.attention(q, k1, v1, scale, out=t["o1"], lse=t["l1"], workspace=None)
+        F.attention(q, k2, v2, scale, out=t["o2"], lse=t["l2"], workspace=None)
+        F.merge([t["o1"], t["o2"]], [t["l1"], t["l2"]], out=t["om"], lse=t["lm"])
+        for x, x8, xs, S in ((q, t["q8"], t["qs"], Sq), (k, t["k8"], t["ks"], Skv),
+                             (v, t["v8"], t["vs"], Skv)):
+            _lib.dit_quant_fp8(x, x8, xs, B, H, S, d)
+        if ws8 is None:
+            ws8 = F.workspace_for(t["q8"], t["k8"], _lib.DIT_DTYPE_FP8_E4M3)
+        F.attention_fp8(t["q8"], t["qs"], t["k8"], t["ks"], t["v8"], t["vs"], scale,
+                        out=t["of"], lse=t["lf"], workspace=ws8)
+        t["la"].copy_(neg_inf)
+        F.attention_acc(q, k1, v1, t["oa"], t["la"], scale, workspace=ws_half)
+        F.attention_acc(q, k2, v2, t["oa"], t["la"], scale, workspace=ws_half)
+
+    eager = bufs()
+    work(eager)
+    torch.cuda.synchronize()
+    for name in ("o", "om", "of", "oa"):
+        assert torch.isfinite(eager[name].float()).all(), name
+
+    say("graph capture: capturing")
+    static = bufs()
+    work(static)  # warm up on the side stream torch captures on
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work(static)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        say(f"graph capture: replay {rep}")
+        for t in static.values():  # outputs poisoned between replays
+            t.view(torch.uint8).fill_(0xFF)
+        other = bufs()  # the program's own eager work in between
+        work(other)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in eager:
+            a, b = static[name], eager[name]
+            same = torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+            assert same, f"replay {rep}: {name} differs from the eager result"
+        for name in ("o", "om", "of", "oa"):
+            assert torch.equal(other[name].view(torch.uint8), eager[name].view(torch.uint8)), name
