@@ -1,8 +1,9 @@
 """The bf16 forward pass at the largest K/V the library accepts.
 
 One batch of K (or V) may hold up to 2^32 - 1 bytes: the kernels address it
-with 32-bit buffer offsets.  Here B1 H1 d128 with Skv = 2^24 - 1 keys, so K and
-V are each 4 GiB - 256 bytes and the last tiles sit right below the limit.
+with 32-bit buffer offsets.  Here B1 H1 with Skv = 2^32 / (2d) - 1 keys (d128:
+2^24 - 1, d64: 2^25 - 1), so K and V are each 4 GiB - 2d bytes and the last
+tiles sit right below the limit.
 
 Expected values in closed form (no pass over 8 GiB on the CPU): every key row
 is the same k0 and every value row the same v0, except a few special keys j
@@ -38,10 +39,11 @@ def _bf16_round(x: np.ndarray) -> np.ndarray:
     return wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
 
 
-def test_fwd_at_the_largest_kv():
-    B, H, d, Sq = 1, 1, 128, 37
-    Skv = (1 << 24) - 1                      # 256 bytes per key: 2^32 - 256 bytes
-    assert Skv * H * d * 2 <= (1 << 32) - 1
+@pytest.mark.parametrize("d", [128, 64])
+def test_fwd_at_the_largest_kv(d):
+    B, H, Sq = 1, 1, 37
+    Skv = (1 << 32) // (2 * d) - 1          # 2d bytes per key: 2^32 - 2d bytes
+    assert (Skv + 1) * H * d * 2 == 1 << 32
     rng = np.random.default_rng(7100)
     scale = float(np.float32(1 / math.sqrt(d)))
     u = rng.standard_normal(d)
@@ -50,7 +52,7 @@ def test_fwd_at_the_largest_kv():
     q = _bf16_round(a[:, None] * u[None] + 0.05 * rng.standard_normal((Sq, d)))
     k0 = _bf16_round(rng.standard_normal(d) / 8)
     v0 = _bf16_round(rng.standard_normal(d))
-    special = [0, 1 << 22, (1 << 23) + 5, Skv - 64, Skv - 2, Skv - 1]
+    special = [0, Skv // 4, Skv // 2 + 5, Skv - 64, Skv - 2, Skv - 1]
     kj = {j: _bf16_round(k0 + (30 + 0.4 * i) / scale * u) for i, j in enumerate(special)}
     vj = {j: _bf16_round(rng.standard_normal(d)) for j in special}
 
