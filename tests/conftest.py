@@ -18,4 +18,10 @@ def _oracle_built():
     import oracle
     if not os.path.exists(oracle._LIB_PATH):
         oracle.build()
+    # the HIP library too, if nothing is built yet (a fresh checkout: built
+    # libraries are not in version control); an existing build is used as is
+    from attention_non_causal_amd import _lib
+    from attention_non_causal_amd import build as libbuild
+    if not os.path.exists(_lib.LIB_PATH) and libbuild.hipcc():
+        libbuild.build()
     yield
