@@ -12,6 +12,8 @@
 // loads and stores are contiguous 1 KiB runs.  All threads of a row sit in
 // the same wavefront, so an in-place merge (o == o_parts[0]) reads every
 // input before any lane of the row writes.
+#include <utility>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -23,68 +25,108 @@ struct MergeKernelArgs {
     const float* lse_parts[kMaxMergeParts];
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeKernelArgs p, int n_parts,
-                                                    uint16_t* O, float* LSE, int H, int Sq,
-                                                    long n_rows)
+// NP (the number of parts) is a template argument so that the part loops
+// unroll: a lane issues the loads of all NP log-sum-exps and all NP chunks
+// before it waits on any of them.  With one 16-byte load in flight per lane
+// (a loop whose trip count is only known at run time waits on each part's
+// load before it issues the next) the 32 waves a CU can hold keep too few
+// bytes in flight to cover HBM latency: the Wan-shape merge ran at 60% of
+// the HBM peak that way.
+template <int D, int NP>
+__global__ __launch_bounds__(256) void merge_kernel(MergeKernelArgs p, uint16_t* O, float* LSE,
+                                                    int H, int Sq, long n_rows)
 {
     constexpr int kChunks = D / 8;
-    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-    const long row = gid / kChunks;
-    const int c = (int)(gid % kChunks);
-    if (row >= n_rows)
+    // 32-bit row arithmetic (the launcher checks that the rows fit): 64-bit
+    // divisions by H and Sq would cost more vector instructions than the rest
+    // of the kernel
+    const unsigned row = blockIdx.x * (256u / kChunks) + threadIdx.x / kChunks;
+    const int c = (int)(threadIdx.x % kChunks);
+    if (row >= (unsigned)n_rows)
         return;
-    const int h = (int)(row % H);
-    const long bs = row / H;
-    const int s = (int)(bs % Sq);
-    const long b = bs / Sq;
-    const long lidx = (b * H + h) * Sq + s;
+    const unsigned bs = row / (unsigned)H;
+    const unsigned h = row - bs * (unsigned)H;
+    const unsigned b = bs / (unsigned)Sq;
+    const unsigned s = bs - b * (unsigned)Sq;
+    const long lidx = ((long)b * H + h) * Sq + s;
+
+    float lse[NP];
+    u32x4 x[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+        lse[i] = p.lse_parts[i][lidx];
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+        x[i] = ld_global16(p.o_parts[i] + (long)row * D + c * 8);
 
     float M = -INFINITY;
-    for (int i = 0; i < n_parts; ++i)
-        M = fmaxf(M, p.lse_parts[i][lidx]);
-
-    u32x4 out = {0, 0, 0, 0};
-    float lse_out = -INFINITY;
-    if (M != -INFINITY) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float L = 0.f;
-        for (int i = 0; i < n_parts; ++i) {
-            const float w = exp2_fast((p.lse_parts[i][lidx] - M) * kLog2e);
-            const u32x4 x = ld_global16(p.o_parts[i] + row * D + c * 8);
-            L += w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += w * __builtin_bit_cast(float, x[e] << 16);
-                acc[2 * e + 1] += w * __builtin_bit_cast(float, x[e] & 0xffff0000u);
-            }
+    for (int i = 0; i < NP; ++i)
+        M = fmaxf(M, lse[i]);
+    // No branch on M: the chunks are used on every path, so the compiler does
+    // not sink their loads behind the wait on the log-sum-exps.  When every
+    // part is empty (M = -inf) the weights are exp2(-inf) = 0 and the result
+    // is selected as O = 0, LSE = -inf below.
+    const bool empty = M == -INFINITY;
+    const float m = empty ? 0.f : M;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const float w = exp2_fast((lse[i] - m) * kLog2e);
+        L += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w * __builtin_bit_cast(float, x[i][e] << 16);
+            acc[2 * e + 1] += w * __builtin_bit_cast(float, x[i][e] & 0xffff0000u);
         }
-        const float inv = 1.f / L;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            out[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-        lse_out = M + log2_fast(L) * kLn2;
     }
-    st_global16(O + row * D + c * 8, out);
+    const float inv = 1.f / L;
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        out[e] = empty ? 0u : pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    const float lse_out = empty ? -INFINITY : M + log2_fast(L) * kLn2;
+    st_global16(O + (long)row * D + c * 8, out);
     if (c == 0)
         LSE[lidx] = lse_out;
+}
+
+template <int D, int NP>
+hipError_t launch_merge_np(const MergeKernelArgs& p, const MergeArgs& a, long n_rows,
+                           unsigned blocks, hipStream_t stream)
+{
+    return launch_kernel(merge_kernel<D, NP>, dim3(blocks), dim3(256), stream, p, a.o, a.lse,
+                         a.H, a.Sq, n_rows);
+}
+
+template <int D, int... NP>
+hipError_t launch_merge_parts(std::integer_sequence<int, NP...>, const MergeKernelArgs& p,
+                              const MergeArgs& a, long n_rows, unsigned blocks,
+                              hipStream_t stream)
+{
+    using Launch = hipError_t (*)(const MergeKernelArgs&, const MergeArgs&, long, unsigned,
+                                  hipStream_t);
+    static constexpr Launch table[] = {&launch_merge_np<D, NP + 1>...};
+    return table[a.n_parts - 1](p, a, n_rows, blocks, stream);
 }
 
 template <int D>
 hipError_t launch_merge_d(const MergeArgs& a, hipStream_t stream)
 {
+    if (a.n_parts < 1 || a.n_parts > kMaxMergeParts)
+        return hipErrorInvalidValue;
     MergeKernelArgs p = {};
     for (int i = 0; i < a.n_parts; ++i) {
         p.o_parts[i] = (const uint16_t*)a.o_parts[i];
         p.lse_parts[i] = a.lse_parts[i];
     }
     const long n_rows = (long)a.B * a.Sq * a.H;
-    const long threads = n_rows * (D / 8);
-    const long blocks = (threads + 255) / 256;
-    if (blocks > 0x7fffffffL)
+    if (n_rows > 0x7fffffffL)
         return hipErrorInvalidConfiguration;
-    return launch_kernel(merge_kernel<D>, dim3((unsigned)blocks), dim3(256), stream, p,
-                         a.n_parts, a.o, a.lse, a.H, a.Sq, n_rows);
+    const long blocks = (n_rows + 256 / (D / 8) - 1) / (256 / (D / 8));
+    return launch_merge_parts<D>(std::make_integer_sequence<int, kMaxMergeParts>(), p, a, n_rows,
+                                 (unsigned)blocks, stream);
 }
 
 }  // namespace
