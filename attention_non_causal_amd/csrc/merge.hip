@@ -32,7 +32,11 @@ struct MergeKernelArgs {
 // load before it issues the next) the 32 waves a CU can hold keep too few
 // bytes in flight to cover HBM latency: the Wan-shape merge ran at 60% of
 // the HBM peak that way.
-template <int D, int NP>
+// NT: non-temporal loads and stores, for merges that move more bytes than
+// the 256 MB last-level cache (MALL) holds -- streaming them through it only
+// evicts other data (Wan-shape merge, 426 MB: +10%); a smaller merge whose
+// partial outputs may still sit there keeps ordinary accesses (-8% with NT).
+template <int D, int NP, bool NT>
 __global__ __launch_bounds__(256) void merge_kernel(MergeKernelArgs p, uint16_t* O, float* LSE,
                                                     int H, int Sq, long n_rows)
 {
@@ -57,7 +61,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeKernelArgs p, uint16_t*
         lse[i] = p.lse_parts[i][lidx];
 #pragma unroll
     for (int i = 0; i < NP; ++i)
-        x[i] = ld_global16(p.o_parts[i] + (long)row * D + c * 8);
+        x[i] = NT ? __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(p.o_parts[i] + (long)row * D + c * 8))
+                  : ld_global16(p.o_parts[i] + (long)row * D + c * 8);
 
     float M = -INFINITY;
 #pragma unroll
@@ -87,7 +93,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeKernelArgs p, uint16_t*
     for (int e = 0; e < 4; ++e)
         out[e] = empty ? 0u : pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
     const float lse_out = empty ? -INFINITY : M + log2_fast(L) * kLn2;
-    st_global16(O + (long)row * D + c * 8, out);
+    if (NT)
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(O + (long)row * D + c * 8));
+    else
+        st_global16(O + (long)row * D + c * 8, out);
     if (c == 0)
         LSE[lidx] = lse_out;
 }
@@ -96,8 +105,13 @@ template <int D, int NP>
 hipError_t launch_merge_np(const MergeKernelArgs& p, const MergeArgs& a, long n_rows,
                            unsigned blocks, hipStream_t stream)
 {
-    return launch_kernel(merge_kernel<D, NP>, dim3(blocks), dim3(256), stream, p, a.o, a.lse,
-                         a.H, a.Sq, n_rows);
+    constexpr long kMallBytes = 256l << 20;
+    const long bytes = (long)(NP + 1) * n_rows * (D * 2 + 4);
+    if (bytes > kMallBytes)
+        return launch_kernel(merge_kernel<D, NP, true>, dim3(blocks), dim3(256), stream, p, a.o,
+                             a.lse, a.H, a.Sq, n_rows);
+    return launch_kernel(merge_kernel<D, NP, false>, dim3(blocks), dim3(256), stream, p, a.o,
+                         a.lse, a.H, a.Sq, n_rows);
 }
 
 template <int D, int... NP>

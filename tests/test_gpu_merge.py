@@ -124,3 +124,40 @@ def test_wan_ring_share_full_size():
     say("wan ring share: oracle (full 32760 keys) on sampled rows")
     o_ref, l_ref = oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
     compare(host_f64(o)[:, rows], host_f64(l)[:, :, rows], o_ref, l_ref, what="wan_ring")
+
+
+@pytest.mark.parametrize("n,d", [(2, 64), (3, 128)])
+def test_merge_larger_than_the_last_level_cache(n, d):
+    """A merge that moves more than 256 MB takes the kernel's streaming
+    (non-temporal) accesses; a slice of its rows, merged on its own, takes the
+    ordinary ones.  The arithmetic is the same, so the two agree bit for bit,
+    and the slice matches the oracle (some rows and parts set to -inf)."""
+    B, H, Sq = 1, 256 if d == 64 else 128, 3000
+    say(f"large merge n{n} d{d}: {(n + 1) * B * Sq * H * (2 * d + 4) / 1e6:.0f} MB")
+    assert (n + 1) * B * Sq * H * (2 * d + 4) > 256 << 20
+    dev = _gpu.device()
+    gen = torch.Generator(device=dev).manual_seed(4000 + n)
+    parts_o = [torch.randn((B, Sq, H, d), device=dev, generator=gen).to(torch.bfloat16)
+               for _ in range(n)]
+    parts_l = [torch.randn((B, H, Sq), device=dev, generator=gen) * 3 + 5 for _ in range(n)]
+    parts_l[0][:, :, 7] = -math.inf
+    for p in parts_l:
+        p[:, 3, 11] = -math.inf
+    o, l = F.merge(parts_o, parts_l)
+    s0, s1 = 5, 40  # rows 5..39 of every head: a small merge of its own
+    so = [p[:, s0:s1].contiguous() for p in parts_o]
+    sl = [p[:, :, s0:s1].contiguous() for p in parts_l]
+    o_s, l_s = F.merge(so, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, s0:s1].view(torch.int16), o_s.view(torch.int16))
+    assert torch.equal(l[:, :, s0:s1], l_s)
+    o_bits = np.stack([p.view(torch.int16).cpu().numpy().view(np.uint16) for p in so])
+    lse = np.stack([p.cpu().numpy() for p in sl])
+    o_ref, l_ref = oracle.attn_merge(o_bits, lse)
+    og, lg = host_f64(o_s), host_f64(l_s)
+    assert (np.abs(og - o_ref) <= _gpu.bf16_ulp(o_ref) + 1e-6).all()
+    fin = np.isfinite(l_ref)
+    assert (np.isneginf(lg) == ~fin).all()
+    empty_rows = np.broadcast_to((~fin).transpose(0, 2, 1)[..., None], og.shape)
+    assert empty_rows.any() and (og[empty_rows] == 0).all()
+    assert np.abs(lg[fin] - l_ref[fin]).max() <= 1e-5 * np.abs(l_ref[fin]).max()
