@@ -48,7 +48,20 @@ def to_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def time_launches(fn, steps, warmup):
+def settle(fn, seconds):
+    """Keep calling fn() for `seconds` of wall time (in batches of 8 between
+    synchronisations).  After a pause -- input generation on the host -- the
+    shader clock takes ~0.1 s of load to settle, longer than a few warmup
+    calls of a short kernel."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_launches(fn, steps, warmup, min_warm_s=0.0):
     """Run fn() warmup times, then time `steps` calls: returns (wall ms per call
     between two synchronisations, list of per-call event ms on torch's current
     stream, which is the stream the library launches on)."""
@@ -56,6 +69,7 @@ def time_launches(fn, steps, warmup):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    settle(fn, min_warm_s)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -69,7 +83,7 @@ def time_launches(fn, steps, warmup):
     return wall, [a.elapsed_time(b) for a, b in ev]
 
 
-def time_batched(fn, steps, warmup):
+def time_batched(fn, steps, warmup, min_warm_s=0.0):
     """ms per call of a short launch: one event pair around `steps` back-to-back
     calls on torch's current stream (per-call event pairs would mostly measure
     launch gaps for kernels of a few tens of microseconds)."""
@@ -77,6 +91,7 @@ def time_batched(fn, steps, warmup):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    settle(fn, min_warm_s)
     stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
@@ -164,6 +179,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0: skip)")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of back-to-back calls before each extra is timed, so the "
+                         "shader clock has settled (0: only the warmup calls)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device-to-device copy of 1 GiB, whose HBM "
                          "counters calibrate FETCH_SIZE / WRITE_SIZE in a --pmc profile")
@@ -202,7 +220,7 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        extras = run_extras(dev, max(3, args.steps // 4), 2)
+        extras = run_extras(dev, max(3, args.steps // 4), 2, args.settle)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -241,7 +259,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def run_extras(dev, steps, warmup):
+def run_extras(dev, steps, warmup, settle_s):
     import numpy as np
     import torch
     from attention_non_causal_amd import _lib, functional as F
@@ -255,7 +273,7 @@ def run_extras(dev, steps, warmup):
         lse = torch.empty((W.B, W.H, W.Sq), dtype=torch.float32, device=dev)
         ws = F.workspace_for(q, k)
         ms = time_batched(lambda: F.attention(q, k, v, W.scale, out=o, lse=lse, workspace=ws),
-                          4 * steps, warmup)
+                          4 * steps, warmup, settle_s)
         res[name] = {"kernel_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1)}
         log(f"extra {name}: {ms:.3f} ms, {res[name]['tflops']} TFLOP/s")
 
@@ -270,9 +288,10 @@ def run_extras(dev, steps, warmup):
     lse = torch.empty((1, W.H, W.Sq), dtype=torch.float32, device=dev)
     wall, evs = time_launches(
         lambda: F.ring_share_attention(q, k, v, W.n_chunks, W.scale, parts=parts, out=o, lse=lse),
-        steps, warmup)
+        steps, warmup, settle_s)
     ms = float(np.mean(evs))
-    mms = time_batched(lambda: F.merge(parts[0], parts[1], out=o, lse=lse), 4 * steps, warmup)
+    mms = time_batched(lambda: F.merge(parts[0], parts[1], out=o, lse=lse), 4 * steps, warmup,
+                       settle_s)
     merge_bytes = W.n_chunks * (W.Sq * W.H * W.d * 2 + W.H * W.Sq * 4) + W.Sq * W.H * W.d * 2 \
         + W.H * W.Sq * 4
     # the same share as a ring loop runs it: each chunk merged into the running
@@ -282,7 +301,7 @@ def run_extras(dev, steps, warmup):
     _, aevs = time_launches(
         lambda: F.ring_share_attention_acc(q, k, v, W.n_chunks, W.scale, out=o, lse=lse,
                                            workspace=aws),
-        steps, warmup)
+        steps, warmup, settle_s)
     ams = float(np.mean(aevs))
     res["wan_ring"] = {"total_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1),
                        "merge_ms": round(mms, 4),
@@ -319,15 +338,13 @@ def run_extras(dev, steps, warmup):
 
     quant_all()
     qms = time_batched(lambda: _lib.dit_quant_fp8(k, bufs["k"][0], bufs["k"][1], W.B, W.H,
-                                                   W.Skv, W.d), 4 * steps, warmup)
+                                                   W.Skv, W.d), 4 * steps, warmup, settle_s)
     qbytes = W.B * W.Skv * W.H * W.d * 3 + nblk * W.B * W.H * 4
     res["quant_fp8"] = {"kernel_ms": round(qms, 4), "GBs": round(qbytes / qms / 1e6, 1)}
     log(f"extra quant_fp8 (one tensor): {qms:.4f} ms = {res['quant_fp8']['GBs']} GB/s")
-    # the fp8 kernel's first launches after the quantiser run slower; time it
-    # after 10 warmup launches, as the other shapes reach steady state in fewer
-    _, aevs = time_launches(attn_fp8, steps, max(warmup, 10))
+    _, aevs = time_launches(attn_fp8, steps, warmup, settle_s)
     ams = float(np.mean(aevs))
-    _, levs = time_launches(lambda: (quant_all(), attn_fp8()), steps, warmup)
+    _, levs = time_launches(lambda: (quant_all(), attn_fp8()), steps, warmup, settle_s)
     lms = float(np.mean(levs))
     res["flux_fp8"] = {"kernel_ms": round(ams, 4), "tflops": round(W.flops / ams / 1e9, 1),
                        "pct_of_fp8_peak": round(100 * W.flops / ams / 1e9 / PEAK_FP8_TFLOPS, 2),
