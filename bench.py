@@ -102,6 +102,29 @@ def time_batched(fn, steps, warmup, min_warm_s=0.0):
     return a.elapsed_time(b) / steps
 
 
+def time_graph(fn, calls, replays, settle_s):
+    """ms per call of `calls` back-to-back fn() captured once into a HIP graph
+    (torch.cuda.CUDAGraph captures the stream the library launches on) and
+    replayed `replays` times between two events."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    settle(graph.replay, settle_s)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * calls)
+
+
 def cpu_baseline(W, g, budget_s):
     """Time the fp64 oracle on a bounded sample of query rows (all heads, all
     keys) of the same workload; report its TFLOP/s."""
@@ -276,6 +299,13 @@ def run_extras(dev, steps, warmup, settle_s):
                           4 * steps, warmup, settle_s)
         res[name] = {"kernel_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1)}
         log(f"extra {name}: {ms:.3f} ms, {res[name]['tflops']} TFLOP/s")
+        if name == "tiny":
+            # a launch-bound shape: the same calls replayed from one captured
+            # HIP graph (no host work per call) against issuing them eagerly
+            gms = time_graph(lambda: F.attention(q, k, v, W.scale, out=o, lse=lse, workspace=ws),
+                             16, max(1, steps // 4), settle_s)
+            res[name]["graph_ms_per_call"] = round(gms, 4)
+            log(f"extra {name}: {gms:.4f} ms per call replayed from a graph of 16 calls")
 
     W = wl.WORKLOADS["wan_ring"]
     g = wl.generate(W)
