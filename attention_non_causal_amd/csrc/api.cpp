@@ -304,7 +304,8 @@ int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, in
         return DIT_ERR_UNSUPPORTED;
     const int64_t o_bytes = checked_bytes({B, Sq, H, d, 2});
     const int64_t lse_bytes = checked_bytes({B, H, Sq, 4});
-    if (o_bytes < 0 || lse_bytes < 0)
+    // the kernel indexes (b, s, h) rows with 32-bit integers
+    if (o_bytes < 0 || lse_bytes < 0 || (int64_t)B * Sq * H > INT32_MAX)
         return DIT_ERR_SHAPE;
     if (!aligned(o, 16) || !aligned(lse, 4))
         return DIT_ERR_ALIGN;

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DIT_ATTN_VERSION 10300 /* major*10000 + minor*100 + patch */
+#define DIT_ATTN_VERSION 10301 /* major*10000 + minor*100 + patch */
 
 enum dit_status {
     DIT_OK = 0,
@@ -182,6 +182,9 @@ int dit_attn_fwd_acc(const void* q, const void* k, const void* v, void* o, float
  *       [B][Sq][H][d] partial outputs and fp32 [B][H][Sq] partial LSEs
  *       (exactly what dit_attn_fwd writes).
  *   n_parts: 1..16.
+ *   B * Sq * H <= 2^31 - 1 rows (DIT_ERR_SHAPE otherwise; the kernel indexes
+ *       rows with 32-bit integers, and a larger part exceeds any one GPU's
+ *       memory for either head dimension).
  *   o, lse: device outputs in the same layouts.  o may be exactly o_parts[0]
  *       and lse exactly lse_parts[0] (in-place merge); any other overlap of an
  *       output with an input returns DIT_ERR_ALIAS.

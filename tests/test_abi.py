@@ -37,7 +37,7 @@ def test_library_exports_header_functions():
 
 
 def test_version_and_status_strings():
-    assert _lib.dit_version() == 10300
+    assert _lib.dit_version() == 10301
     texts = [_lib.dit_status_string(s) for s in range(9)]
     assert len(set(texts)) == 9 and all(texts)
     assert _lib.dit_status_string(99) == "unknown status"
@@ -101,6 +101,7 @@ def merge(o_parts=None, lse_parts=None, n=2, o=O, lse=L, B=1, H=2, Sq=100, d=64)
                                        DIT_ERR_UNSUPPORTED),
     (dict(d=32), DIT_ERR_UNSUPPORTED),
     (dict(B=0), DIT_ERR_SHAPE), (dict(Sq=-1), DIT_ERR_SHAPE),
+    (dict(B=2, Sq=1 << 15, H=1 << 15), DIT_ERR_SHAPE),  # 2^31 rows: one past the limit
     (dict(o=O + 4), DIT_ERR_ALIGN), (dict(lse=L + 1), DIT_ERR_ALIGN),
     (dict(o_parts=[Q, K + 8]), DIT_ERR_ALIGN),
     (dict(o=K + 256), DIT_ERR_ALIAS),           # partial overlap with part 1
