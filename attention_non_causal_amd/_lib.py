@@ -194,8 +194,9 @@ def dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_
 
 def dit_attn_fwd_acc(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,
                      kv_batch_tokens=0, workspace=None, workspace_bytes=0, stream=None) -> None:
-    """The bf16 forward pass over one key block merged into the running
-    (o, lse) (see the header)."""
+    """The forward pass over one key block merged into the running (o, lse)
+    (see the header).  fp8: q, k, v are fp8_tensor descriptors and
+    kv_batch_tokens must be 0."""
     _check(dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype,
                                    kv_batch_tokens, workspace, workspace_bytes, stream))
 

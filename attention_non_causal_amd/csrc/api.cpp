@@ -132,7 +132,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
         return DIT_ERR_NULL;
     if (dtype != DIT_DTYPE_BF16 && dtype != DIT_DTYPE_FP8_E4M3)
         return DIT_ERR_UNSUPPORTED;
-    if (acc && dtype != DIT_DTYPE_BF16)
+    // fp8 key blocks are tensors of their own (with their own block scales):
+    // no batch stride
+    if (acc && dtype != DIT_DTYPE_BF16 && kv_batch_tokens != 0)
         return DIT_ERR_UNSUPPORTED;
     if (d != 64 && d != 128)
         return DIT_ERR_UNSUPPORTED;

@@ -12,6 +12,12 @@
 // the bytes are reproducible bit for bit.  |x * inv| <= 448 * (1 + 2^-23), which
 // rounds to 448, so no value reaches the saturation range.
 //
+// Non-finite input: a NaN takes no part in amax and encodes as 0x7F (e4m3's
+// NaN, sign cleared); an infinity makes amax, and so the block's scale,
+// infinite, which turns every finite value of the block into a (signed) zero
+// and the infinity itself (inf * 0) into 0x7F.  A block whose values are all
+// zero or NaN has amax = 0: scale 1 and every byte 0.
+//
 // One workgroup per block: the block's 128 x d bf16 values are read once into
 // registers (16-byte loads, consecutive threads on consecutive chunks), the
 // magnitude maximum is reduced across the workgroup, and the same registers
@@ -23,6 +29,22 @@ namespace dit {
 namespace {
 
 constexpr int kBlockTokens = 128;
+
+// bf16 magnitude bits m (sign cleared) as they count towards amax: a NaN
+// (above the infinity's 0x7f80) counts as zero.
+__device__ __forceinline__ uint32_t amax_mag(uint32_t m)
+{
+    return m <= 0x7f80u ? m : 0u;
+}
+
+// Four e4m3 codes with the sign bit of every NaN code (S.1111.111) cleared,
+// so that a NaN encodes as 0x7F whatever the conversion made of its sign (no
+// finite code has all seven low bits set).
+__device__ __forceinline__ uint32_t nan_codes_positive(uint32_t w)
+{
+    const uint32_t nan = ((w & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+    return w & ~nan;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ X,
@@ -45,7 +67,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     const long base = ((b * S + s0) * H + h) * D;
 
     u32x4 v[kPer];
-    uint32_t amax_bits = 0;  // max of |x| as bf16 magnitude bits (monotone in |x|)
+    uint32_t amax_bits = 0;  // max of |x| as bf16 magnitude bits (monotone in |x|), NaN left out
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int c = tid + 256 * i;
@@ -56,8 +78,8 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
             v[i] = ld_global16(X + base + r * tok + cc * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            amax_bits = max(amax_bits, v[i][e] & 0x7fffu);
-            amax_bits = max(amax_bits, (v[i][e] >> 16) & 0x7fffu);
+            amax_bits = max(amax_bits, amax_mag(v[i][e] & 0x7fffu));
+            amax_bits = max(amax_bits, amax_mag((v[i][e] >> 16) & 0x7fffu));
         }
     }
 #pragma unroll
@@ -92,7 +114,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
                 const float f3 = __builtin_bit_cast(float, x1 & 0xffff0000u) * inv;
                 int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
                 packed = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, packed, true);
-                w[half] = (uint32_t)packed;
+                w[half] = nan_codes_positive((uint32_t)packed);
             }
         }
         *reinterpret_cast<u32x2*>(X8 + base + r * tok + cc * 8) = w;

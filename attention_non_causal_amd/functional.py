@@ -2,12 +2,32 @@
 
 Marshalling only -- the computation is the library's HIP kernels.  Tensors
 are contiguous [B, S, H, d] on a ROCm device; LSE is fp32 [B, H, Sq].
+
+``stream``: None (torch's current stream), a torch stream, or a raw HIP stream
+handle (0: the null stream).  Every allocation a helper makes (outputs,
+workspaces) and every fill happens on that same stream, so the caching
+allocator and the kernels agree on the order of the work.
 """
 from __future__ import annotations
 
+import contextlib
 import math
 
 from . import _lib
+
+
+def _on_stream(stream, device):
+    """(context manager making `stream` torch's current stream, the stream
+    argument to pass to the binding)."""
+    import torch
+    if stream is None:
+        return contextlib.nullcontext(), None
+    if isinstance(stream, int):
+        ts = torch.cuda.ExternalStream(stream, device=device) if stream else \
+            torch.cuda.default_stream(device)
+    else:
+        ts = stream
+    return torch.cuda.stream(ts), ts
 
 
 def _require(t, dtype, name):
@@ -44,21 +64,23 @@ def attention(q, k, v, scale: float | None = None, out=None, lse=None, stream=No
     Skv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        _lib.dit_attn_fwd(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
-                          stream)
-        return out, lse
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
-        workspace = workspace_for(q, k)
-    n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _lib.dit_attn_fwd_ws(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
-                         workspace, n_bytes, stream)
+    ctx, stream = _on_stream(stream, q.device)
+    with ctx:
+        if out is None:
+            out = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            _lib.dit_attn_fwd(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                              stream)
+            return out, lse
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+            workspace = workspace_for(q, k)
+        n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _lib.dit_attn_fwd_ws(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                             workspace, n_bytes, stream)
     return out, lse
 
 
@@ -68,10 +90,12 @@ def quantize_fp8(x, stream=None):
     import torch
     _require(x, torch.bfloat16, "x")
     B, S, H, d = x.shape
-    x8 = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
-    nblk = (S + _lib.DIT_FP8_BLOCK - 1) // _lib.DIT_FP8_BLOCK
-    sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
-    _lib.dit_quant_fp8(x, x8, sc, B, H, S, d, stream)
+    ctx, stream = _on_stream(stream, x.device)
+    with ctx:
+        x8 = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
+        nblk = (S + _lib.DIT_FP8_BLOCK - 1) // _lib.DIT_FP8_BLOCK
+        sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+        _lib.dit_quant_fp8(x, x8, sc, B, H, S, d, stream)
     return x8, sc
 
 
@@ -86,24 +110,26 @@ def attention_fp8(q8, q_scale, k8, k_scale, v8, v_scale, scale: float | None = N
     Skv = k8.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
     dq = _lib.fp8_tensor(q8, q_scale)
     dk = _lib.fp8_tensor(k8, k_scale)
     dv = _lib.fp8_tensor(v8, v_scale)
-    if workspace is None:
-        _lib.dit_attn_fwd(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale,
-                          _lib.DIT_DTYPE_FP8_E4M3, stream)
-        return out, lse
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
-        workspace = workspace_for(q8, k8, _lib.DIT_DTYPE_FP8_E4M3)
-    n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _lib.dit_attn_fwd_ws(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale,
-                         _lib.DIT_DTYPE_FP8_E4M3, workspace, n_bytes, stream)
+    ctx, stream = _on_stream(stream, q8.device)
+    with ctx:
+        if out is None:
+            out = torch.empty((B, Sq, H, d), dtype=torch.bfloat16, device=q8.device)
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
+        if workspace is None:
+            _lib.dit_attn_fwd(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale,
+                              _lib.DIT_DTYPE_FP8_E4M3, stream)
+            return out, lse
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+            workspace = workspace_for(q8, k8, _lib.DIT_DTYPE_FP8_E4M3)
+        n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _lib.dit_attn_fwd_ws(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale,
+                             _lib.DIT_DTYPE_FP8_E4M3, workspace, n_bytes, stream)
     return out, lse
 
 
@@ -111,11 +137,13 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
     """LSE-merge of partial results (lists of bf16 [B,Sq,H,d] / fp32 [B,H,Sq])."""
     import torch
     B, Sq, H, d = o_parts[0].shape
-    if out is None:
-        out = torch.empty_like(o_parts[0])
-    if lse is None:
-        lse = torch.empty_like(lse_parts[0])
-    _lib.dit_attn_merge(o_parts, lse_parts, len(o_parts), out, lse, B, H, Sq, d, stream)
+    ctx, stream = _on_stream(stream, o_parts[0].device)
+    with ctx:
+        if out is None:
+            out = torch.empty_like(o_parts[0])
+        if lse is None:
+            lse = torch.empty_like(lse_parts[0])
+        _lib.dit_attn_merge(o_parts, lse_parts, len(o_parts), out, lse, B, H, Sq, d, stream)
     return out, lse
 
 
@@ -137,14 +165,42 @@ def attention_acc(q, k, v, out, lse, scale: float | None = None, stream=None,
         Skv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
-        n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d, _lib.DIT_DTYPE_BF16)
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
-    n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _lib.dit_attn_fwd_acc(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
-                          kv_batch_tokens, workspace, n_bytes, stream)
+    ctx, stream = _on_stream(stream, q.device)
+    with ctx:
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+            n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, Skv, d, _lib.DIT_DTYPE_BF16)
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+        n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _lib.dit_attn_fwd_acc(q, k, v, out, lse, B, H, Sq, Skv, d, scale, _lib.DIT_DTYPE_BF16,
+                              kv_batch_tokens, workspace, n_bytes, stream)
+    return out, lse
+
+
+def attention_fp8_acc(q8, q_scale, k8, k_scale, v8, v_scale, out, lse,
+                      scale: float | None = None, stream=None, workspace="auto"):
+    """Merge fp8 attention over one key block (its own e4m3 tensor and block
+    scales, from quantize_fp8) into the running result (out, lse) over earlier
+    keys (dit_attn_fwd_acc with DIT_DTYPE_FP8_E4M3): rows whose lse is -inf
+    have no keys yet.  workspace as for attention."""
+    import torch
+    B, Sq, H, d = q8.shape
+    Skv = k8.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = _lib.fp8_tensor(q8, q_scale)
+    dk = _lib.fp8_tensor(k8, k_scale)
+    dv = _lib.fp8_tensor(v8, v_scale)
+    ctx, stream = _on_stream(stream, q8.device)
+    with ctx:
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+            workspace = workspace_for(q8, k8, _lib.DIT_DTYPE_FP8_E4M3)
+        n_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _lib.dit_attn_fwd_acc(dq, dk, dv, out, lse, B, H, Sq, Skv, d, scale,
+                              _lib.DIT_DTYPE_FP8_E4M3, 0, workspace, n_bytes, stream)
     return out, lse
 
 
@@ -154,28 +210,31 @@ def ring_share_attention_acc(q, k, v, n_chunks: int, scale: float | None = None,
     empty (lse = -inf) and each of ``n_chunks`` consecutive KV chunks is merged
     into it as it is processed (dit_attn_fwd_acc on pointer offsets into k/v,
     batches Skv tokens apart, so any B) -- no partial outputs, no separate
-    merge."""
+    merge.  The reset of lse, the allocations and the launches all run on
+    ``stream``."""
     import torch
     B, Sq, H, d = q.shape
     Skv = k.shape[1]
     if Skv % n_chunks:
         raise ValueError("Skv must be a multiple of n_chunks")
     c = Skv // n_chunks
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
-        n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, c, d, _lib.DIT_DTYPE_BF16)
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
-    lse.fill_(-math.inf)
-    es = k.element_size()
-    for i in range(n_chunks):
-        off = i * c * H * d * es
-        attention_acc(q, (k.data_ptr() + off, c), (v.data_ptr() + off, c), out, lse, scale,
-                      stream, workspace, kv_batch_tokens=Skv)
+    ctx, stream = _on_stream(stream, q.device)
+    with ctx:
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+            n = _lib.dit_attn_fwd_workspace_size(B, H, Sq, c, d, _lib.DIT_DTYPE_BF16)
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+        lse.fill_(-math.inf)
+        es = k.element_size()
+        for i in range(n_chunks):
+            off = i * c * H * d * es
+            attention_acc(q, (k.data_ptr() + off, c), (v.data_ptr() + off, c), out, lse, scale,
+                          stream, workspace, kv_batch_tokens=Skv)
     return out, lse
 
 
@@ -195,15 +254,17 @@ def ring_share_attention(q, k, v, n_chunks: int, scale: float | None = None, par
     c = Skv // n_chunks
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if parts is None:
-        o_parts = [torch.empty_like(q) for _ in range(n_chunks)]
-        lse_parts = [torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-                     for _ in range(n_chunks)]
-    else:
-        o_parts, lse_parts = parts
-    es = k.element_size()
-    for i in range(n_chunks):
-        off = i * c * H * d * es
-        _lib.dit_attn_fwd(q, k.data_ptr() + off, v.data_ptr() + off, o_parts[i], lse_parts[i],
-                          B, H, Sq, c, d, scale, _lib.DIT_DTYPE_BF16, stream)
-    return merge(o_parts, lse_parts, out, lse, stream)
+    ctx, stream = _on_stream(stream, q.device)
+    with ctx:
+        if parts is None:
+            o_parts = [torch.empty_like(q) for _ in range(n_chunks)]
+            lse_parts = [torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+                         for _ in range(n_chunks)]
+        else:
+            o_parts, lse_parts = parts
+        es = k.element_size()
+        for i in range(n_chunks):
+            off = i * c * H * d * es
+            _lib.dit_attn_fwd(q, k.data_ptr() + off, v.data_ptr() + off, o_parts[i],
+                              lse_parts[i], B, H, Sq, c, d, scale, _lib.DIT_DTYPE_BF16, stream)
+        return merge(o_parts, lse_parts, out, lse, stream)

@@ -48,6 +48,90 @@ def to_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def host_info():
+    """Host CPU model, ROCm version and HIP runtime of this run."""
+    import torch
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    return {"cpu_model": cpu, "host_threads": len(os.sched_getaffinity(0)),
+            "rocm_version": rocm, "hip_runtime": torch.version.hip}
+
+
+def _smi_gfx_clock_mhz():
+    """The GPU's current shader (gfx) clock in MHz from amd-smi, or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                           text=True, timeout=10)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    if r.returncode != 0:
+        return None
+    try:
+        data = json.loads(r.stdout)
+    except ValueError:
+        return None
+    # the "gfx_*" entries of the clock section; each has a current clock value
+    vals = []
+
+    def walk(x, key=""):
+        if isinstance(x, dict):
+            for k, v in x.items():
+                walk(v, f"{key}/{k}")
+        elif isinstance(x, list):
+            for v in x:
+                walk(v, key)
+        elif re.search(r"gfx_?\d*/clk$", key) and isinstance(x, (int, float)):
+            vals.append(float(x))
+        elif re.search(r"gfx_?\d*/clk/value$", key) and isinstance(x, (int, float)):
+            vals.append(float(x))
+    walk(data)
+    return float(sum(vals) / len(vals)) if vals else None
+
+
+def sustained_clock(fn, seconds):
+    """Run fn() back to back for `seconds` (untimed, after the measurement)
+    while a host thread samples the shader clock with amd-smi; returns
+    (median MHz over the samples, number of samples) or (None, 0)."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        time.sleep(0.2)  # let the load start
+        while not stop.is_set():
+            c = _smi_gfx_clock_mhz()
+            if c is None:
+                return
+            samples.append(c)
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None, 0
+    samples.sort()
+    return samples[len(samples) // 2], len(samples)
+
+
 def settle(fn, seconds):
     """Keep calling fn() for `seconds` of wall time (in batches of 8 between
     synchronisations).  After a pause -- input generation on the host -- the
@@ -190,7 +274,7 @@ def bench_fwd(W, g, dev, steps, warmup):
     torch.cuda.synchronize()
     cold = a.elapsed_time(b)
     wall, evs = time_launches(fn, steps, warmup)
-    return wall, evs, cold
+    return wall, evs, cold, fn
 
 
 def main():
@@ -205,6 +289,12 @@ def main():
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of back-to-back calls before each extra is timed, so the "
                          "shader clock has settled (0: only the warmup calls)")
+    ap.add_argument("--clock-seconds", type=float, default=1.5,
+                    help="seconds of back-to-back steps after the timed ones while amd-smi "
+                         "samples the shader clock (0: skip)")
+    ap.add_argument("--fp8-rows", type=int, default=64,
+                    help="query rows of the fp8 workloads compared with the oracle in the "
+                         "cpu_baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device-to-device copy of 1 GiB, whose HBM "
                          "counters calibrate FETCH_SIZE / WRITE_SIZE in a --pmc profile")
@@ -233,7 +323,7 @@ def main():
     W = wl.WORKLOADS[args.workload]
     log(f"{props.name}: {props.multi_processor_count} CUs; workload {W.name}: generating inputs")
     g = wl.generate(W)
-    wall, evs, cold_ms = bench_fwd(W, g, dev, args.steps, args.warmup)
+    wall, evs, cold_ms, step_fn = bench_fwd(W, g, dev, args.steps, args.warmup)
     kern_ms = float(np.mean(evs))
     value = W.flops / (wall * 1e-3) / 1e12
     achieved = W.flops / (kern_ms * 1e-3) / 1e12
@@ -241,15 +331,26 @@ def main():
         f"(median {float(np.median(evs)):.3f}, min {min(evs):.3f}, first launch "
         f"{cold_ms:.3f}) -> {achieved:.1f} TFLOP/s")
 
+    # the shader clock this step sustains (after the timed steps; amd-smi
+    # sampled from a host thread while the step runs back to back)
+    clock_mhz, clock_n = (None, 0)
+    if args.clock_seconds > 0:
+        clock_mhz, clock_n = sustained_clock(step_fn, args.clock_seconds)
+        log(f"sustained shader clock: {clock_mhz} MHz ({clock_n} amd-smi samples)")
+
     extras = {}
+    fp8_outputs = None
     if not args.no_extras:
-        extras = run_extras(dev, max(3, args.steps // 4), 2, args.settle)
+        extras, fp8_outputs = run_extras(dev, max(3, args.steps // 4), 2, args.settle)
 
     cpu = None
     if args.cpu_budget > 0:
         log("cpu_baseline: timing the oracle on a row sample")
         cpu = cpu_baseline(W, g, args.cpu_budget)
         log(f"cpu_baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+        if fp8_outputs is not None:
+            extras["flux_fp8"].update(fp8_errors(fp8_outputs, args.fp8_rows))
+            extras["flux_fp8_unit_normal"] = fp8_unit_normal_error(W, g, dev, args.fp8_rows)
 
     out = {
         "metric": "attention TFLOP/s & % of MFMA peak, B1 H24 S=16896 d128 bf16",
@@ -276,7 +377,12 @@ def main():
                      "kernel_ms_min": round(float(min(evs)), 4),
                      "first_launch_ms": round(cold_ms, 4)},
         "cpu_baseline": cpu,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "cus": props.multi_processor_count,
+                   "sustained_sclk_mhz": clock_mhz, "sclk_samples": clock_n,
+                   "peak_basis": "2.5 PFLOP/s bf16 / 5.0 PFLOP/s fp8 dense at 2.4 GHz, "
+                                 "256 CUs"},
+        "host": host_info(),
         "extras": extras,
     }
     print(json.dumps(out), flush=True)
@@ -348,7 +454,6 @@ def run_extras(dev, steps, warmup, settle_s):
     W = wl.WORKLOADS["flux_fp8"]
     g = wl.generate(W)
     q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)
-    del g
     nblk = (W.Skv + 127) // 128
     bufs = {n: (torch.empty(t.shape, dtype=torch.uint8, device=dev),
                 torch.empty((W.B, W.H, nblk), dtype=torch.float32, device=dev))
@@ -367,6 +472,7 @@ def run_extras(dev, steps, warmup, settle_s):
                         bufs["v"][1], W.scale, out=o, lse=lse, workspace=ws8)
 
     quant_all()
+    torch.cuda.synchronize()
     qms = time_batched(lambda: _lib.dit_quant_fp8(k, bufs["k"][0], bufs["k"][1], W.B, W.H,
                                                    W.Skv, W.d), 4 * steps, warmup, settle_s)
     qbytes = W.B * W.Skv * W.H * W.d * 3 + nblk * W.B * W.H * 4
@@ -383,7 +489,72 @@ def run_extras(dev, steps, warmup, settle_s):
     log(f"extra flux_fp8: attention {ams:.3f} ms = {res['flux_fp8']['tflops']} TFLOP/s "
         f"({res['flux_fp8']['pct_of_fp8_peak']}% of fp8 peak); with 3 quantiser launches "
         f"{lms:.3f} ms")
-    return res
+    # the outputs of the last timed call (the path is deterministic), kept for
+    # the comparison with the oracle in the cpu_baseline leg
+    torch.cuda.synchronize()
+    fp8_out = {"W": W, "g": g, "o": o.float().cpu().numpy(), "lse": lse.cpu().numpy(),
+               "q8": bufs["q"][0].cpu().numpy(), "qs": bufs["q"][1].cpu().numpy(),
+               "k8": bufs["k"][0].cpu().numpy(), "ks": bufs["k"][1].cpu().numpy(),
+               "v8": bufs["v"][0].cpu().numpy(), "vs": bufs["v"][1].cpu().numpy()}
+    return res, fp8_out
+
+
+def fp8_errors(out, n_rows):
+    """cpu_baseline leg, outside any timed region: the fp8 path's output on the
+    x8-outlier FLUX-like workload against the oracle on sampled query rows (all
+    heads and keys) -- max|dO| and max|dLSE| against the oracle on the
+    unquantised bf16 inputs (the path's total error), against the oracle on
+    the dequantised inputs (the kernel's own error), and the quantisation
+    floor (the two oracles against each other)."""
+    import numpy as np
+    import oracle
+    from attention_non_causal_amd import workloads as wl
+    W, g = out["W"], out["g"]
+    rows = wl.sample_rows(W.Sq, n_rows)
+    log(f"flux_fp8 vs oracle on {len(rows)} rows")
+    o_ref, l_ref = oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
+    deq = [oracle.dequant_fp8(out[n + "8"], out[n + "s"]) for n in "qkv"]
+    o_dq, l_dq = oracle.attn_fwd(deq[0], deq[1], deq[2], W.scale, rows=rows)
+    o, l = out["o"][:, rows].astype(np.float64), out["lse"][:, :, rows].astype(np.float64)
+    r = {"oracle_rows": int(len(rows)),
+         "max_dO_vs_unquantised": float(np.abs(o - o_ref).max()),
+         "max_dLSE_vs_unquantised": float(np.abs(l - l_ref).max()),
+         "max_dO_vs_dequantised": float(np.abs(o - o_dq).max()),
+         "max_dLSE_vs_dequantised": float(np.abs(l - l_dq).max()),
+         "floor_max_dO": float(np.abs(o_dq - o_ref).max()),
+         "floor_max_dLSE": float(np.abs(l_dq - l_ref).max())}
+    log(f"flux_fp8 errors: {r}")
+    return r
+
+
+def fp8_unit_normal_error(W, g, dev, n_rows):
+    """cpu_baseline leg: the fp8 path (quantiser + split forward) on the
+    unit-normal FLUX-like inputs against the oracle on the unquantised inputs
+    -- the 6e-2 gate -- on sampled rows, with the quantisation floor."""
+    import numpy as np
+    import oracle
+    import torch
+    from attention_non_causal_amd import functional as F
+    from attention_non_causal_amd import workloads as wl
+    q, k, v = to_dev(g["q"], dev), to_dev(g["k"], dev), to_dev(g["v"], dev)
+    q8, qs = F.quantize_fp8(q)
+    k8, ks = F.quantize_fp8(k)
+    v8, vs = F.quantize_fp8(v)
+    o, lse = F.attention_fp8(q8, qs, k8, ks, v8, vs, W.scale)
+    torch.cuda.synchronize()
+    rows = wl.sample_rows(W.Sq, n_rows)
+    log(f"flux fp8 unit-normal vs oracle on {len(rows)} rows")
+    o_ref, l_ref = oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
+    deq = [oracle.dequant_fp8(a.cpu().numpy(), b.cpu().numpy())
+           for a, b in ((q8, qs), (k8, ks), (v8, vs))]
+    o_dq, _ = oracle.attn_fwd(deq[0], deq[1], deq[2], W.scale, rows=rows)
+    og = o.float().cpu().numpy()[:, rows].astype(np.float64)
+    lg = lse.cpu().numpy()[:, :, rows].astype(np.float64)
+    r = {"oracle_rows": int(len(rows)), "max_dO_vs_unquantised": float(np.abs(og - o_ref).max()),
+         "max_dLSE_vs_unquantised": float(np.abs(lg - l_ref).max()),
+         "floor_max_dO": float(np.abs(o_dq - o_ref).max()), "gate_max_dO": 6e-2}
+    log(f"flux fp8 unit-normal errors: {r}")
+    return r
 
 
 if __name__ == "__main__":

@@ -140,18 +140,22 @@ int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * dit_attn_fwd_acc -- the bf16 forward pass over one block of keys, merged
- * into a running result over the key blocks before it: what a rank of ring
- * attention runs each time a KV block arrives ("xDiT 项目概述" sec. 3.2: the
- * ring dimension splits the sequence into blocks passed around the GPUs, and
- * each GPU combines the partial results), without writing partial outputs or
+ * dit_attn_fwd_acc -- the forward pass over one block of keys, merged into a
+ * running result over the key blocks before it: what a rank of ring attention
+ * runs each time a KV block arrives ("xDiT 项目概述" sec. 3.2: the ring
+ * dimension splits the sequence into blocks passed around the GPUs, and each
+ * GPU combines the partial results), without writing partial outputs or
  * running a separate merge.
  *
  *   Arguments as dit_attn_fwd_ws (workspace rules included: the split launch
  *   is used when dit_attn_fwd_workspace_size is not 0), except:
- *   dtype: DIT_DTYPE_BF16 only (fp8: DIT_ERR_UNSUPPORTED).
- *   kv_batch_tokens: tokens between the starts of consecutive batches in k
- *       and v (0: Skv, contiguous).  With B > 1 the key block is usually a
+ *   dtype: DIT_DTYPE_BF16, or DIT_DTYPE_FP8_E4M3 with q, k, v host
+ *       dit_fp8_tensor_t descriptors as for dit_attn_fwd; an fp8 key block is
+ *       a tensor of its own with its own block scales [B][H][ceil(Skv/128)]
+ *       (as dit_quant_fp8 writes them for that block), so kv_batch_tokens
+ *       must be 0 for fp8 (DIT_ERR_UNSUPPORTED otherwise).
+ *   kv_batch_tokens (bf16): tokens between the starts of consecutive batches
+ *       in k and v (0: Skv, contiguous).  With B > 1 the key block is usually a
  *       slice [s0, s0 + Skv) of larger [B][S][H][d] tensors: pass k, v offset
  *       by s0 tokens and kv_batch_tokens = S.  Must be 0 or >= Skv (else
  *       DIT_ERR_SHAPE); the batches' extents are checked for aliasing.
@@ -199,7 +203,10 @@ int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, in
  *     inv   = fp32(448 / amax),  x8 = e4m3_rne(fp32(x * inv))
  *     scale = fp32(amax / 448)                   (amax == 0: scale 1, x8 = 0)
  * Every fp32 step is a single correctly rounded operation, so the output is
- * bit-reproducible.
+ * bit-reproducible.  Non-finite input: a NaN takes no part in amax and encodes
+ * as 0x7F; an infinity makes amax and the block's scale +inf, so the block's
+ * finite values encode as (signed) zeros and its infinities as 0x7F; a block
+ * whose values are all zero or NaN gets scale 1 and all-zero bytes.
  *   x: device bf16 [B][S][H][d];  x_fp8: device e4m3 [B][S][H][d];
  *   scale: device fp32 [B][H][ceil(S/128)].  Outputs must not overlap x.
  */

@@ -310,7 +310,11 @@ int oracle_attn_merge(const double* o_parts, const double* lse_parts, int n,
  *   scale = fp32(amax / 448)            (amax = 0: scale = 1, q = 0)
  * so that x ~= decode(q) * scale.  x is bf16 [B,S,H,d]; q is e4m3 bytes in
  * the same layout; scale is fp32 [B,H,ceil(S/128)].  The fp32 steps are
- * single correctly rounded IEEE operations, written as such here.          */
+ * single correctly rounded IEEE operations, written as such here.
+ * Non-finite input follows from these steps as written: a NaN fails the
+ * comparison with amax and so takes no part in it, and encodes as 0x7F; an
+ * infinity makes amax infinite, inv = 0 and scale = +inf, so finite values
+ * encode as signed zeros and the infinity (inf * 0 = NaN) as 0x7F.          */
 int oracle_quant_fp8(const uint16_t* x, uint8_t* q, float* scale,
                      int B, int H, int S, int d)
 {

@@ -199,10 +199,19 @@ def test_fwd_acc_kv_batch_stride_checks():
     assert fwd_acc(B=2, o=o_in_k) != DIT_ERR_ALIAS
 
 
-def test_fwd_acc_is_bf16_only():
-    """The merge into a running result exists for the bf16 path only; the fp8
-    dtype is refused before its descriptors are even read."""
-    assert fwd_acc(dtype=DIT_DTYPE_FP8_E4M3) == DIT_ERR_UNSUPPORTED
+def test_fwd_acc_fp8_checks():
+    """fp8 key blocks are tensors of their own: a batch stride is refused
+    before the descriptors are even read (fake addresses here); with
+    descriptors the fp8 checks of dit_attn_fwd apply."""
+    assert fwd_acc(dtype=DIT_DTYPE_FP8_E4M3, kv_batch_tokens=512) == DIT_ERR_UNSUPPORTED
+    good = [_lib.fp8_tensor(Q, Q + (1 << 30)), _lib.fp8_tensor(K, K + (1 << 30)),
+            _lib.fp8_tensor(V, V + (1 << 30))]
+    assert fwd_acc(q=_lib.fp8_tensor(None, Q + (1 << 30)), k=good[1], v=good[2],
+                   dtype=DIT_DTYPE_FP8_E4M3) == DIT_ERR_NULL
+    assert fwd_acc(q=good[0], k=good[1], v=_lib.fp8_tensor(V, V + (1 << 30) + 2),
+                   dtype=DIT_DTYPE_FP8_E4M3) == DIT_ERR_ALIGN
+    assert fwd_acc(q=good[0], k=good[1], v=good[2], o=K + 4096,
+                   dtype=DIT_DTYPE_FP8_E4M3) == DIT_ERR_ALIAS
 
 
 def test_workspace_size_argument_checks():
@@ -218,3 +227,4 @@ def test_workspace_size_argument_checks():
     # the fp8 path plans its split like the bf16 one (on the device's CU count)
     st, _ = _lib.dit_attn_fwd_workspace_size_status(1, 2, 256, 256, 64, DIT_DTYPE_FP8_E4M3)
     assert st in (_lib.DIT_OK, _lib.DIT_ERR_HIP)
+

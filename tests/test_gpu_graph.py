@@ -7,7 +7,12 @@ two-part merge, the fp8 quantiser with the fp8 split forward, and a chain of
 two dit_attn_fwd_acc blocks whose running LSE is reset by a copy (no memset is
 recorded).  It is replayed several times with the program's own eager work
 and synchronisations in between; every replay must reproduce the eager results
-bit for bit (the kernels are deterministic).
+bit for bit (the kernels are deterministic) and match the fp64 oracle: the bf16
+outputs within max|dO| <= 1e-2 / max|dLSE| <= 1e-3 of the oracle over all keys,
+the fp8 output within its per-element bound against the oracle on the
+dequantised inputs.  A second graph holds the Wan-like ring share as a ring
+loop runs it (LSE reset by a fill kernel, four dit_attn_fwd_acc chunks) at full
+size, each replay checked against the oracle over all 32760 keys.
 """
 import math
 
@@ -15,21 +20,23 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from attention_non_causal_amd import _lib, functional as F, workloads as wl
-from tests._gpu import dev_bf16, say
+from tests import _gpu
+from tests._gpu import compare, dev_bf16, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
 
 def _inputs(B, H, Sq, Skv, d, seed):
     g = wl.generate("tiny", seed=seed, B=B, H=H, Sq=Sq, Skv=Skv, d=d)
-    return dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"])
+    return g, (dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"]))
 
 
 def test_graph_replays_match_eager():
     B, H, Sq, Skv, d = 1, 2, 256, 2048, 128
     say("graph capture: inputs and eager results")
-    q, k, v = _inputs(B, H, Sq, Skv, d, seed=6000)
+    g, (q, k, v) = _inputs(B, H, Sq, Skv, d, seed=6000)
     scale = 0.088
     dev = q.device
     ws = F.workspace_for(q, k)
@@ -98,6 +105,26 @@ def test_graph_replays_match_eager():
         work(static)
     torch.cuda.synchronize()
 
+    # the oracle: attention over all keys (the split forward, the merge of the
+    # two halves and the accumulated chain all compute it), and the fp8 path's
+    # reference on the dequantised inputs with its per-element bound
+    from tests.test_gpu_fp8 import dequant, kernel_bound, lse_bound
+    o_ref, l_ref = oracle.attn_fwd(g["q"], g["k"], g["v"], scale)
+    qd8, kd8, vd8 = dequant(g["q"]), dequant(g["k"]), dequant(g["v"])
+    o8_ref, l8_ref = oracle.attn_fwd(qd8, kd8, vd8, scale)
+    bound8 = kernel_bound(qd8, kd8, vd8, scale)
+    lbound8 = lse_bound(qd8, kd8, scale)
+
+    def check_oracle(t, what):
+        for o_name, l_name in (("o", "l"), ("om", "lm"), ("oa", "la")):
+            compare(host_f64(t[o_name]), host_f64(t[l_name]), o_ref, l_ref,
+                    what=f"{what} {o_name}")
+        err8 = np.abs(host_f64(t["of"]) - o8_ref)
+        say(f"{what} of: max|dO| {err8.max():.3e} (worst err/bound {(err8 / bound8).max():.3f})")
+        assert (err8 <= bound8).all(), f"{what}: fp8 output outside its bound"
+        assert (np.abs(host_f64(t["lf"]) - l8_ref) <= lbound8).all()
+
+    check_oracle(eager, "eager")
     for rep in range(3):
         say(f"graph capture: replay {rep}")
         for t in static.values():  # outputs poisoned between replays
@@ -113,3 +140,46 @@ def test_graph_replays_match_eager():
             assert same, f"replay {rep}: {name} differs from the eager result"
         for name in ("o", "om", "of", "oa"):
             assert torch.equal(other[name].view(torch.uint8), eager[name].view(torch.uint8)), name
+        check_oracle(static, f"replay {rep}")
+
+
+def test_graph_wan_ring_share_accumulated_against_oracle():
+    """The Wan-like ring share (B1 H40 d128, 8190 queries, 4 chunks of 8190
+    keys) captured as a ring loop runs it -- the running LSE reset to -inf by a
+    fill kernel, then four dit_attn_fwd_acc launches -- and replayed three
+    times with eager work in between; every replay against the oracle over all
+    32760 keys on 264 rows (the first query tile and 8 more)."""
+    W = wl.WORKLOADS["wan_ring"]
+    say("graph wan ring share: generating inputs")
+    g = wl.generate(W)
+    q, k, v = dev_bf16(g["q"]), dev_bf16(g["k"]), dev_bf16(g["v"])
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty((1, W.H, W.Sq), dtype=torch.float32, device=dev)
+    n = _lib.dit_attn_fwd_workspace_size(1, W.H, W.Sq, W.chunk, W.d)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+
+    def share():
+        F.ring_share_attention_acc(q, k, v, W.n_chunks, W.scale, out=o, lse=lse, workspace=ws)
+
+    share()  # warm up on the side stream torch captures on
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        share()
+    torch.cuda.synchronize()
+    rows = _gpu.tile_rows(W.Sq, (0,), extra=8)
+    say(f"graph wan ring share: oracle on {len(rows)} rows")
+    o_ref, l_ref = oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
+    scratch_o = torch.empty_like(o)
+    for rep in range(3):
+        say(f"graph wan ring share: replay {rep}")
+        o.view(torch.uint8).fill_(0xFF)
+        lse.fill_(float("nan"))
+        F.attention(q[:, :512].contiguous(), k[:, :512].contiguous(), v[:, :512].contiguous(),
+                    W.scale, out=scratch_o[:, :512])  # the program's own eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare(host_f64(o)[:, rows], host_f64(lse)[:, :, rows], o_ref, l_ref,
+                what=f"graph wan replay {rep}")

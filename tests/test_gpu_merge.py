@@ -120,8 +120,9 @@ def test_wan_ring_share_full_size():
     say("wan ring share: 4 chunk forwards + merge")
     o, l = F.ring_share_attention(q, k, v, W.n_chunks, W.scale)
     torch.cuda.synchronize()
-    rows = wl.sample_rows(W.Sq, 16)
-    say("wan ring share: oracle (full 32760 keys) on sampled rows")
+    # the last query tile (254 rows: 8190 = 31 * 256 + 254) and 8 more rows
+    rows = _gpu.tile_rows(W.Sq, (31,), extra=8)
+    say(f"wan ring share: oracle (full 32760 keys) on {len(rows)} rows")
     o_ref, l_ref = oracle.attn_fwd(g["q"], g["k"], g["v"], W.scale, rows=rows)
     compare(host_f64(o)[:, rows], host_f64(l)[:, :, rows], o_ref, l_ref, what="wan_ring")
 

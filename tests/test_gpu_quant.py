@@ -50,3 +50,16 @@ def test_quant_flux_fp8_full_size():
         q_ref, s_ref = oracle.quant_fp8(g[n])
         np.testing.assert_array_equal(s_gpu, s_ref)
         np.testing.assert_array_equal(q_gpu, q_ref)
+
+
+def test_quant_nonfinite_input_matches_oracle():
+    """NaNs (both signs, with a payload), infinities and an all-NaN-and-zero
+    block: bytes and scales identical to the oracle's (NaN out of amax and
+    encoded 0x7F; an infinite amax gives scale +inf and signed zeros)."""
+    from tests.test_oracle_fp8 import _nonfinite_blocks
+    say("quant non-finite input")
+    x = _nonfinite_blocks()
+    q_gpu, s_gpu = _gpu_quant(x)
+    q_ref, s_ref = oracle.quant_fp8(x)
+    np.testing.assert_array_equal(s_gpu, s_ref)
+    np.testing.assert_array_equal(q_gpu, q_ref)

@@ -158,3 +158,71 @@ def test_dequant_inverts_within_bound():
     rel = np.abs(xr - xf) / np.maximum(np.abs(xf), 1e-30)
     big = np.abs(xf) > 0.5
     assert rel[big].max() <= 2.0 ** -4 + 1e-6
+
+
+def _nonfinite_blocks():
+    """bf16 [1, 384, 3, 64]: head 0 block 0 holds NaNs of both signs among
+    finite values, head 1 block 1 a +inf and a -inf, head 2 block 2 only NaNs
+    and zeros; every other block is finite."""
+    x = wl.normal_bf16((1, 384, 3, 64), 310)
+    x[0, 3, 0, 5] = 0x7FC0                    # +NaN
+    x[0, 70, 0, 0] = 0xFFC1                   # -NaN with a payload
+    x[0, 130, 1, 9] = 0x7F80                  # +inf
+    x[0, 200, 1, 2] = 0xFF80                  # -inf
+    x[0, 256:, 2] = 0
+    x[0, 300, 2, 1] = 0x7FC0
+    return x
+
+
+def test_quantiser_nonfinite_input():
+    """The quantiser's steps as written decide non-finite input: a NaN fails
+    the comparison with amax (no part in it) and encodes as 0x7F; an infinity
+    makes amax and the scale +inf, so finite values become signed zeros and the
+    infinities (inf * 0 = NaN) 0x7F; a block of zeros and NaNs has amax 0."""
+    x = _nonfinite_blocks()
+    q, sc = oracle.quant_fp8(x)
+    xf = oracle.bf16_bits_to_f64(x)
+    # NaN block: the same bytes and scale as with its NaNs replaced by zeros,
+    # except 0x7F at the NaNs
+    x0 = x.copy()
+    x0[0, 3, 0, 5] = 0
+    x0[0, 70, 0, 0] = 0
+    q0, s0 = oracle.quant_fp8(x0)
+    assert sc[0, 0, 0] == s0[0, 0, 0]
+    fin = np.isfinite(xf[0, :128, 0])
+    assert (q[0, :128, 0][fin] == q0[0, :128, 0][fin]).all()
+    assert q[0, 3, 0, 5] == 0x7F and q[0, 70, 0, 0] == 0x7F
+    # infinity block: scale +inf, finite values -> signed zeros, infinities -> 0x7F
+    assert sc[0, 1, 1] == np.inf
+    blk, qb = xf[0, 128:256, 1], q[0, 128:256, 1]
+    fin = np.isfinite(blk)
+    assert (qb[fin] == np.where(np.signbit(blk[fin]), 0x80, 0x00)).all()
+    assert (qb[~fin] == 0x7F).all() and (~fin).sum() == 2
+    # zeros and NaNs only: amax = 0, scale 1, all bytes 0
+    assert sc[0, 2, 2] == 1.0 and (q[0, 256:, 2] == 0).all()
+    # the finite blocks are untouched by their neighbours
+    xc = x.copy()
+    xc[0, 3, 0, 5] = xc[0, 70, 0, 0] = xc[0, 130, 1, 9] = xc[0, 200, 1, 2] = 0
+    xc[0, 256:, 2] = wl.normal_bf16((1, 128, 64), 311)
+    qc, scc = oracle.quant_fp8(xc)
+    for h, t in ((0, 1), (0, 2), (1, 0), (1, 2), (2, 0), (2, 1)):
+        sl = slice(128 * t, 128 * (t + 1))
+        assert sc[0, h, t] == scc[0, h, t]
+        np.testing.assert_array_equal(q[0, sl, h], qc[0, sl, h])
+
+
+def test_dequant_closed_form():
+    """dequant(q, scale)[b, s, h, c] = decode(q[b, s, h, c]) * scale[b, h, s // 128],
+    re-derived with NumPy indexing on codes and scales drawn independently (every
+    (b, h, block) has its own scale, so a wrong block, head or batch index shows)."""
+    rng = np.random.default_rng(77)
+    B, S, H, d = 2, 300, 3, 16
+    q = rng.integers(0, 256, size=(B, S, H, d), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x11                 # no NaN codes
+    nblk = (S + 127) // 128
+    sc = rng.uniform(0.5, 4.0, size=(B, H, nblk)).astype(np.float32)
+    got = oracle.dequant_fp8(q, sc)
+    table = oracle.e4m3_decode_table()
+    blk = np.arange(S) // 128
+    scale_bshd = sc.transpose(0, 2, 1)[:, blk, :, None].astype(np.float64)  # [B, S, H, 1]
+    np.testing.assert_array_equal(got, table[q] * scale_bshd)

@@ -43,6 +43,10 @@ FP8_PINS = [
     tf.test_quantiser_matches_torch_cast,
     tf.test_quantiser_blocks_are_independent_and_zero_block,
 ]
+DEQUANT_PINS = [
+    tf.test_dequant_inverts_within_bound,
+    tf.test_dequant_closed_form,
+]
 
 # (name, original text, mutated text, pins expected to catch it)
 MUTANTS = [
@@ -69,6 +73,18 @@ MUTANTS = [
     ("quant_inverse_scale", "inv = 448.0f / famax;", "inv = 440.0f / famax;", FP8_PINS),
     ("quant_block_len", "int s1 = s0 + ORACLE_FP8_BLOCK < S ? s0 + ORACLE_FP8_BLOCK : S;",
      "int s1 = s0 + 64 < S ? s0 + 64 : S;", FP8_PINS),
+    # the dequantiser defines the reference of every fp8 kernel-error test
+    ("dequant_block_index",
+     "double sc = (double)scale[((long)b * H + h) * nblk + s / ORACLE_FP8_BLOCK];",
+     "double sc = (double)scale[((long)b * H + h) * nblk];", DEQUANT_PINS),
+    ("dequant_head_stride",
+     "double sc = (double)scale[((long)b * H + h) * nblk + s / ORACLE_FP8_BLOCK];",
+     "double sc = (double)scale[((long)b * H) * nblk + s / ORACLE_FP8_BLOCK];", DEQUANT_PINS),
+    ("dequant_batch_stride",
+     "double sc = (double)scale[((long)b * H + h) * nblk + s / ORACLE_FP8_BLOCK];",
+     "double sc = (double)scale[((long)h) * nblk + s / ORACLE_FP8_BLOCK];", DEQUANT_PINS),
+    ("dequant_no_scale", "x[t * d + c] = oracle_e4m3_decode(q[t * d + c]) * sc;",
+     "x[t * d + c] = oracle_e4m3_decode(q[t * d + c]);", DEQUANT_PINS),
 ]
 
 
