@@ -30,6 +30,7 @@ DIT_DTYPE_BF16 = 0
 DIT_DTYPE_FP8_E4M3 = 1
 DIT_FP8_BLOCK = 128
 MAX_MERGE_PARTS = 16
+DIT_NOALLOC_SCRATCH_BYTES = 33 << 20
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -66,6 +67,8 @@ def load():
     lib.dit_attn_fwd_workspace_size.restype = I
     lib.dit_attn_fwd_ws.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
     lib.dit_attn_fwd_ws.restype = I
+    lib.dit_attn_fwd_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.dit_attn_fwd_noalloc.restype = I
     lib.dit_attn_fwd_acc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, ctypes.c_longlong, P,
                                      ctypes.c_size_t, P]
     lib.dit_attn_fwd_acc.restype = I
@@ -179,6 +182,23 @@ def dit_attn_fwd_ws(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF
     of workgroups is split over the keys and merged."""
     _check(dit_attn_fwd_ws_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, workspace,
                                   workspace_bytes, stream))
+
+
+def dit_attn_fwd_noalloc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale,
+                               dtype=DIT_DTYPE_BF16, stream=None) -> int:
+    """Call dit_attn_fwd_noalloc and return its status code (no exception)."""
+    args = [_fwd_operand(t, dtype) for t in (q, k, v)]
+    return load().dit_attn_fwd_noalloc(args[0], args[1], args[2], _addr(o), _addr(lse), int(B),
+                                       int(H), int(Sq), int(Skv), int(d), float(scale),
+                                       int(dtype), _stream(stream))
+
+
+def dit_attn_fwd_noalloc(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,
+                         stream=None) -> None:
+    """dit_attn_fwd_ws with the library's static per-GPU scratch instead of a
+    workspace: allocates nothing (calls overlapping on one GPU race)."""
+    _check(dit_attn_fwd_noalloc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype,
+                                       stream))
 
 
 def dit_attn_fwd_acc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype=DIT_DTYPE_BF16,

@@ -121,12 +121,18 @@ int check_fwd_shape(int B, int H, int Sq, int Skv, int d, int dtype)
     return DIT_OK;
 }
 
-// dit_attn_fwd, dit_attn_fwd_ws and dit_attn_fwd_acc; with_ws selects the
-// split launch, acc the merge into the running result held in o, lse, and
-// kv_batch_tokens (acc only; 0: Skv) the distance between batches of k, v.
-int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int Sq, int Skv, int d, float scale, int dtype, bool with_ws, void* ws,
-             size_t ws_bytes, bool acc, long long kv_batch_tokens, hipStream_t stream)
+}  // namespace
+
+namespace dit {
+
+// dit_attn_fwd, dit_attn_fwd_ws, dit_attn_fwd_acc and dit_attn_fwd_noalloc;
+// with_ws selects the split launch, acc the merge into the running result held
+// in o, lse, and kv_batch_tokens (acc only; 0: Skv) the distance between
+// batches of k, v.
+int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Sq, int Skv, int d, float scale, int dtype, bool with_ws, void* ws,
+              size_t ws_bytes, bool acc, long long kv_batch_tokens, hipStream_t stream,
+              void* (*resolve_ws)(int* status))
 {
     if (!q || !k || !v || !o || !lse)
         return DIT_ERR_NULL;
@@ -223,7 +229,15 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
         split = dtype == DIT_DTYPE_BF16 ? dit::plan_fwd_bf16_split(B, H, Sq, Skv, d, n_cu)
                                         : dit::plan_fwd_fp8_split(B, H, Sq, Skv, d, n_cu);
         if (split.n_tail > 0) {
-            if (!ws || ws_bytes < split.ws_bytes || !aligned(ws, 16))
+            if (ws_bytes < split.ws_bytes)
+                return DIT_ERR_WORKSPACE;
+            if (resolve_ws) {
+                int rs = DIT_OK;
+                ws = resolve_ws(&rs);
+                if (rs != DIT_OK)
+                    return rs;
+            }
+            if (!ws || !aligned(ws, 16))
                 return DIT_ERR_WORKSPACE;
             const Range rw = range(ws, (int64_t)split.ws_bytes);
             for (const Range& in : inputs)
@@ -247,15 +261,15 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     return map_hip(dit::launch_fwd_bf16(a, split, stream));
 }
 
-}  // namespace
+}  // namespace dit
 
 extern "C" {
 
 int dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int Sq, int Skv, int d, float scale, int dtype, hipStream_t stream)
 {
-    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, false, nullptr, 0, false, 0,
-                    stream);
+    return dit::fwd_entry(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, false, nullptr, 0,
+                          false, 0, stream, nullptr);
 }
 
 int dit_attn_fwd_workspace_size(int B, int H, int Sq, int Skv, int d, int dtype, size_t* bytes)
@@ -279,8 +293,8 @@ int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
                     int H, int Sq, int Skv, int d, float scale, int dtype, void* workspace,
                     size_t workspace_bytes, hipStream_t stream)
 {
-    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
-                    workspace_bytes, false, 0, stream);
+    return dit::fwd_entry(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
+                          workspace_bytes, false, 0, stream, nullptr);
 }
 
 int dit_attn_fwd_acc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -288,8 +302,8 @@ int dit_attn_fwd_acc(const void* q, const void* k, const void* v, void* o, float
                      long long kv_batch_tokens, void* workspace, size_t workspace_bytes,
                      hipStream_t stream)
 {
-    return fwd_impl(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
-                    workspace_bytes, true, kv_batch_tokens, stream);
+    return dit::fwd_entry(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype, true, workspace,
+                          workspace_bytes, true, kv_batch_tokens, stream, nullptr);
 }
 
 int dit_attn_merge(const void* const* o_parts, const float* const* lse_parts, int n_parts,

@@ -61,6 +61,16 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdSplit& split, hipStream_t 
 FwdSplit plan_fwd_fp8_split(int B, int H, int Sq, int Skv, int d, int n_cu);
 hipError_t launch_fwd_fp8(const FwdArgs& a, const FwdSplit& split, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+// The validated forward entry shared by dit_attn_fwd, _ws, _acc and _noalloc
+// (api.cpp): with_ws selects the split launch (scratch ws of ws_bytes), acc
+// the merge into the running result, kv_batch_tokens the batch distance of k, v.
+// resolve_ws (may be null): called for the scratch address, once every other
+// argument has been validated and only when the launch is split.
+int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Sq, int Skv, int d, float scale, int dtype, bool with_ws, void* ws,
+              size_t ws_bytes, bool acc, long long kv_batch_tokens, hipStream_t stream,
+              void* (*resolve_ws)(int* status));
+
 hipError_t launch_quant_fp8(const void* x, void* x8, float* scale, int B, int H, int S, int d,
                             hipStream_t stream);
 

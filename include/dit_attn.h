@@ -32,9 +32,10 @@
  *   fastest.  LSE [B][H][Sq] fp32.  bf16 is IEEE bfloat16 bits; e4m3 is OCP
  *   E4M3FN (bias 7, max 448, no infinities).
  *   Ownership: the caller owns every buffer.  The library allocates nothing,
- *   keeps no state between calls, never synchronises, and only enqueues work
- *   on `stream` (0 = the null stream), so every call can be captured into a
- *   HIP graph.  Calls are thread-safe.
+ *   keeps no state between calls (dit_attn_fwd_noalloc aside: its static
+ *   scratch array, see there), never synchronises, and only enqueues work on
+ *   `stream` (0 = the null stream), so every call can be captured into a HIP
+ *   graph.  Calls are thread-safe (dit_attn_fwd_noalloc: see there).
  *   Errors: every argument is validated on the host before any HIP call, so an
  *   invalid call returns its status code without touching the device.  A
  *   launch failure returns DIT_ERR_HIP.  Faults inside a kernel surface, as
@@ -138,6 +139,30 @@ int dit_attn_fwd_workspace_size(int B, int H, int Sq, int Skv, int d, int dtype,
 int dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Sq, int Skv, int d, float scale, int dtype,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dit_attn_fwd_noalloc -- dit_attn_fwd_ws without a workspace argument and
+ * without any allocation: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The split launch's scratch is a static device array of
+ * DIT_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its device address is looked up once per device,
+ * on the first split call made with that device current).
+ *
+ *   Arguments and results as dit_attn_fwd_ws (bf16 or fp8), minus the
+ *   workspace.  DIT_NOALLOC_SCRATCH_BYTES covers every shape on a GPU of up to
+ *   256 compute units; where a shape's split needs more, the call returns
+ *   DIT_ERR_WORKSPACE (and enqueues nothing).
+ *   Every call on one GPU shares that GPU's scratch array: calls that may
+ *   overlap on one GPU (other streams, other host threads) race and must be
+ *   serialised by the caller.  Nothing in the array needs clearing between
+ *   calls.
+ */
+#define DIT_NOALLOC_SCRATCH_BYTES (33u << 20)
+
+int dit_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Sq, int Skv, int d, float scale, int dtype,
+                         hipStream_t stream);
 
 /*
  * dit_attn_fwd_acc -- the forward pass over one block of keys, merged into a

@@ -25,8 +25,8 @@ def fwd(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
 def test_library_exports_header_functions():
     names = _lib.header_functions()
     assert set(names) == {"dit_attn_fwd", "dit_attn_fwd_workspace_size", "dit_attn_fwd_ws",
-                          "dit_attn_fwd_acc", "dit_attn_merge", "dit_quant_fp8",
-                          "dit_status_string", "dit_version"}
+                          "dit_attn_fwd_noalloc", "dit_attn_fwd_acc", "dit_attn_merge",
+                          "dit_quant_fp8", "dit_status_string", "dit_version"}
     lib = _lib.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -228,3 +228,34 @@ def test_workspace_size_argument_checks():
     st, _ = _lib.dit_attn_fwd_workspace_size_status(1, 2, 256, 256, 64, DIT_DTYPE_FP8_E4M3)
     assert st in (_lib.DIT_OK, _lib.DIT_ERR_HIP)
 
+
+def noalloc(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=256, Skv=256, d=64, scale=0.125,
+            dtype=DIT_DTYPE_BF16):
+    return _lib.dit_attn_fwd_noalloc_status(q, k, v, o, lse, B, H, Sq, Skv, d, scale, dtype,
+                                            stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), DIT_ERR_NULL), (dict(lse=None), DIT_ERR_NULL),
+    (dict(dtype=2), DIT_ERR_UNSUPPORTED), (dict(d=96), DIT_ERR_UNSUPPORTED),
+    (dict(B=0), DIT_ERR_SHAPE), (dict(Skv=-1), DIT_ERR_SHAPE),
+    (dict(scale=0.0), DIT_ERR_VALUE), (dict(scale=math.nan), DIT_ERR_VALUE),
+    (dict(k=K + 2), DIT_ERR_ALIGN), (dict(o=Q + 4096), DIT_ERR_ALIAS),
+])
+def test_noalloc_rejects_before_any_hip_call(kw, status):
+    """dit_attn_fwd_noalloc validates every argument before its first HIP call
+    (the device query and the scratch lookup come after), so on a host without
+    a GPU an invalid call returns its own status."""
+    assert noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size_constant():
+    """The Python constant mirrors DIT_NOALLOC_SCRATCH_BYTES, which covers the
+    largest split any shape needs on a GPU of 256 compute units: 512 pieces of
+    128 rows x (128 + 2) fp32 (fp8, d = 128)."""
+    import re
+    text = open(_lib.HEADER_PATH).read()
+    m = re.search(r"#define DIT_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.DIT_NOALLOC_SCRATCH_BYTES
+    assert _lib.DIT_NOALLOC_SCRATCH_BYTES >= 512 * 128 * 130 * 4
+    assert _lib.DIT_NOALLOC_SCRATCH_BYTES >= 256 * 256 * 129 * 4
