@@ -4,8 +4,9 @@ The bf16 kernel issues its matrix instructions as inline asm (so that the O
 and row-sum accumulators stay in AGPRs and the slot order holds); the
 compiler's hazard recognizer does not look inside an asm statement, so the
 wait states between a matrix instruction and vector instructions touching its
-registers are the kernel's own responsibility.  (The fp8 kernel's MFMAs are
-compiler-generated; it is checked the same way.)  This test compiles each
+registers are the kernel's own responsibility.  The fp8 kernel issues its P·V
+MFMA as inline asm for the same reason (its QK^T and row-sum MFMAs are
+compiler-generated and checked the same way).  This test compiles each
 source to assembly with the library's own flags and checks, on the
 straight-line code:
 
@@ -133,7 +134,7 @@ def test_no_unprotected_mfma_hazards(name):
     problems = []
     for name, body in kernels:
         n_mfma = sum(1 for ins in body if ins[0].startswith("v_mfma"))
-        assert n_mfma >= 8, name
+        assert n_mfma >= 4, name
         problems += [f"{name}: {p}" for p in _check(body)]
     assert not problems, "\n".join(problems[:20])
 
