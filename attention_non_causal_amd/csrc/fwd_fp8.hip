@@ -113,13 +113,14 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c, 
 // O^T block += A B in place (A scale 1, B scale 2^(scale_b - 127)), as an asm
 // statement: the compiler otherwise writes each product to fresh registers and
 // keeps the old accumulator alive beside it.  The compiler does not see this as
-// an MFMA, so the kernel keeps the wait states itself (acc_wait before vector
-// code touches the accumulator, acc_written after it writes it;
-// tests/test_asm_hazards.py checks the generated code).
+// an MFMA, so the kernel keeps the wait states itself: the statement opens
+// with two (the compiler may set up an operand, such as the scale, with a
+// vector move just before it), and acc_wait comes before vector code touches
+// the accumulator (tests/test_asm_hazards.py checks the generated code).
 __device__ __forceinline__ void mfma_fp8_acc(f32x16& acc, const i32x8& a, const i32x8& b,
                                              int scale_b)
 {
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                  : "+v"(acc)
                  : "v"(a), "v"(b), "v"(127), "v"(scale_b));
 }
@@ -135,13 +136,6 @@ __device__ __forceinline__ void acc_wait(f32x16 (&acc)[MB])
                      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
     else
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
-}
-
-// 2 wait states after vector code wrote an accumulator, before the next asm
-// MFMA reads it.
-__device__ __forceinline__ void acc_written(f32x16& acc)
-{
-    asm volatile("s_nop 1" : "+v"(acc));
 }
 
 // D(16x16) = A(16x128 e4m3) B(128x16 e4m3), unit scales.  Operand layout per
@@ -398,10 +392,8 @@ struct FwdFp8Tile {
             lr_run *= alpha;
             acc_wait(oacc);  // after the last P.V MFMAs on O
 #pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
+            for (int mb = 0; mb < kMB; ++mb)
                 oacc[mb] *= alpha;
-                acc_written(oacc[mb]);
-            }
             lsum = weigh_pack(pw, c, m_used - lift);
         }
         const float inv_fk = __builtin_amdgcn_rcpf(vmant * Cfg::kPScale);

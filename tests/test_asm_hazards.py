@@ -14,7 +14,8 @@ straight-line code:
   C or a scale operand) is at least 2 wait states before it;
 * a vector instruction reading or writing an MFMA's destination, or writing
   its C operand, comes at least 18 wait states after a bf16 32x32x16 MFMA
-  (8 passes; 11 are needed) and 19 after an fp8 32x32x64 one (16 passes).
+  (8 passes; 11 are needed), 19 after an fp8 32x32x64 one (16 passes) and 11
+  after an fp8 16x16x128 one (8 passes).
 
 Wait states are counted conservatively: 1 per instruction, N+1 for s_nop N,
 4 for an MFMA issue.  Only CPU is needed (hipcc cross-compiles).
@@ -31,6 +32,7 @@ SOURCES = ("fwd_bf16.hip", "fwd_fp8.hip")
 VALU_TO_MFMA = 2
 MFMA_TO_VALU = 18      # 8-pass v_mfma_f32_32x32x16_bf16 (needs 11)
 MFMA16_TO_VALU = 19    # 16-pass v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3)
+MFMA8_SCALE_TO_VALU = 11  # 8-pass v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3)
 
 _REG = re.compile(r"^([va])(?:\[(\d+):(\d+)\]|(\d+))$")
 
@@ -89,6 +91,8 @@ def _cost(ins):
 
 
 def _after(op):
+    if op.startswith("v_mfma_scale_f32_16x16x128"):
+        return MFMA8_SCALE_TO_VALU
     return MFMA16_TO_VALU if op.startswith("v_mfma_scale") else MFMA_TO_VALU
 
 
