@@ -8,12 +8,14 @@ been built, the first call raises ``LibraryNotBuilt`` -- nothing falls back.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libditattn.so")
+DEBUG_LIB_PATH = os.path.join(_PKG, "libditattn_debugsync.so")  # race-check build (tests only)
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dit_attn.h")
 
 DIT_OK = 0
@@ -55,11 +57,30 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    _lib = _open(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path):
+    """Route every call of this module to another build of the library (the
+    race-check variant libditattn_debugsync.so, for the tests) inside the
+    block, then back."""
+    global _lib
+    saved = load()
+    _lib = _open(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _open(path):
+    if not os.path.exists(path):
         raise LibraryNotBuilt(
-            f"{LIB_PATH} is missing: build it with `python -m attention_non_causal_amd.build` "
+            f"{path} is missing: build it with `python -m attention_non_causal_amd.build` "
             "(or __graft_entry__.build()); there is no fallback implementation")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.dit_attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.dit_attn_fwd.restype = I
@@ -80,7 +101,6 @@ def load():
     lib.dit_status_string.restype = ctypes.c_char_p
     lib.dit_version.argtypes = []
     lib.dit_version.restype = I
-    _lib = lib
     return lib
 
 

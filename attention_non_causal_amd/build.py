@@ -2,6 +2,10 @@
 
 Each source is compiled to an object under _build/ (in parallel), then linked
 into attention_non_causal_amd/libditattn.so.  Run as a module or call build().
+
+build(debug_barriers=True) builds the race-check variant libditattn_debugsync.so
+from the same sources with -DDIT_DEBUG_BARRIERS (see debug_sync in
+csrc/common.hpp); only tests load it.
 """
 from __future__ import annotations
 
@@ -19,6 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build", "ditattn")
 LIB_NAME = "libditattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+DEBUG_BUILD_DIR = os.path.join(ROOT, "_build", "ditattn_debugsync")
+DEBUG_LIB_PATH = os.path.join(PKG, "libditattn_debugsync.so")
 ARCH = "gfx950"
 
 
@@ -53,21 +59,25 @@ FILE_FLAGS = {
 }
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, extra: tuple = ()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = ([hipcc()] + COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + list(extra)
+           + ["-c", src, "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, debug_barriers: bool = False) -> str:
+    build_dir = DEBUG_BUILD_DIR if debug_barriers else BUILD_DIR
+    lib_path = DEBUG_LIB_PATH if debug_barriers else LIB_PATH
+    extra = ("-DDIT_DEBUG_BARRIERS",) if debug_barriers else ()
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s_: _compile(s_, build_dir, extra), srcs))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -75,12 +85,13 @@ def build(verbose: bool = False) -> str:
     # resolve every symbol now: a kernel whose host stub was not emitted shows
     # up here as an undefined symbol instead of at the first load on a GPU host
     ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, debug_barriers=True)
     sys.exit(0)

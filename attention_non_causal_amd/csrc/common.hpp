@@ -158,6 +158,23 @@ __device__ __forceinline__ void wait_vmem_all()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Race check.  Built with -DDIT_DEBUG_BARRIERS, the forward kernels end every
+// step of their key loop with this: every outstanding memory operation of the
+// wave waited for, then a workgroup barrier.  The waves of a workgroup then
+// run in lock step and every copy into LDS has landed before anyone goes on,
+// so a race between waves (an LDS slot read before its copy landed, or
+// overwritten while still read) cannot happen in that build.  The arithmetic
+// is the same in both builds, so any difference between their results points
+// at such a race (tests/test_gpu_debug_barriers.py compares them bit for bit).
+// In the normal build it is empty.
+__device__ __forceinline__ void debug_sync()
+{
+#ifdef DIT_DEBUG_BARRIERS
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __syncthreads();
+#endif
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

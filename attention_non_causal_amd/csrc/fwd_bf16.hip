@@ -571,6 +571,7 @@ struct FwdBf16Tile {
             fold<P, kSlots - 1>();
         l_run += lsum;
         lsum_max = fmaxf(lsum_max, lsum);
+        debug_sync();
     }
 };
 

@@ -436,6 +436,7 @@ struct FwdFp8Tile {
         if (j < n_it)
             valu_phase(j);
         phase_barrier();
+        debug_sync();
     }
 };
 

@@ -24,4 +24,6 @@ def _oracle_built():
     from attention_non_causal_amd import build as libbuild
     if not os.path.exists(_lib.LIB_PATH) and libbuild.hipcc():
         libbuild.build()
+    if not os.path.exists(_lib.DEBUG_LIB_PATH) and libbuild.hipcc():
+        libbuild.build(debug_barriers=True)
     yield

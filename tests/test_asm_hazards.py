@@ -47,13 +47,13 @@ def _regs(tok):
     return {(kind, i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
 
 
-def _asm(name):
+def _asm(name, extra=()):
     try:
         libbuild.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
     out = subprocess.run(
-        [libbuild.hipcc()] + libbuild.COMMON_FLAGS + libbuild.FILE_FLAGS.get(name, [])
+        [libbuild.hipcc()] + libbuild.COMMON_FLAGS + libbuild.FILE_FLAGS.get(name, []) + list(extra)
         + ["--cuda-device-only", "-S", os.path.join(libbuild.CSRC, name), "-o", "-"],
         capture_output=True, text=True, check=True)
     return out.stdout
@@ -153,3 +153,15 @@ def test_checker_flags_a_planted_hazard():
     assert len(bad) == 2, bad
     assert _check([body[0], ["s_nop", "1"], body[1], ["s_nop", "7"], ["s_nop", "7"],
                    ["s_nop", "7"], body[2]]) == []
+
+
+@pytest.mark.parametrize("name", SOURCES)
+def test_debug_barrier_build_adds_barriers(name):
+    """The race-check build (-DDIT_DEBUG_BARRIERS, libditattn_debugsync.so) has
+    more workgroup barriers in each forward kernel than the normal build."""
+    def barriers(text):
+        return {k: sum(1 for ins in body if ins[0] == "s_barrier") for k, body in _kernels(text)}
+    normal, debug = barriers(_asm(name)), barriers(_asm(name, ("-DDIT_DEBUG_BARRIERS",)))
+    assert normal.keys() == debug.keys() and len(normal) == 2
+    for k in normal:
+        assert debug[k] > normal[k], (k, normal[k], debug[k])
