@@ -69,6 +69,30 @@ def host_info():
             "rocm_version": rocm, "hip_runtime": torch.version.hip}
 
 
+def _smi_market_name():
+    """The GPU's product name from amd-smi (torch reports a generic one), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "static", "-g", "0", "-a", "--json"], capture_output=True,
+                           text=True, timeout=10)
+        data = json.loads(r.stdout) if r.returncode == 0 else None
+    except (OSError, subprocess.TimeoutExpired, ValueError):
+        return None
+    found = []
+
+    def walk(x):
+        if isinstance(x, dict):
+            for k, v in x.items():
+                if k == "market_name" and isinstance(v, str) and v.strip():
+                    found.append(v.strip())
+                walk(v)
+        elif isinstance(x, list):
+            for v in x:
+                walk(v)
+    walk(data)
+    return found[0] if found else None
+
+
 def _smi_gfx_clock_mhz():
     """The GPU's current shader (gfx) clock in MHz from amd-smi, or None."""
     import re
@@ -295,6 +319,10 @@ def main():
     ap.add_argument("--fp8-rows", type=int, default=64,
                     help="query rows of the fp8 workloads compared with the oracle in the "
                          "cpu_baseline leg")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the benchmark: the dense matrix-core throughput this GPU "
+                         "sustains (bf16 and e4m3, random and all-zero operands; "
+                         "libditprobe.so) and its shader clock meanwhile; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device-to-device copy of 1 GiB, whose HBM "
                          "counters calibrate FETCH_SIZE / WRITE_SIZE in a --pmc profile")
@@ -311,6 +339,9 @@ def main():
 
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling(dev, props)), flush=True)
+        return
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -377,7 +408,8 @@ def main():
                      "kernel_ms_min": round(float(min(evs)), 4),
                      "first_launch_ms": round(cold_ms, 4)},
         "cpu_baseline": cpu,
-        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+        "device": {"name": _smi_market_name() or props.name, "torch_name": props.name,
+                   "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count,
                    "sustained_sclk_mhz": clock_mhz, "sclk_samples": clock_n,
                    "peak_basis": "2.5 PFLOP/s bf16 / 5.0 PFLOP/s fp8 dense at 2.4 GHz, "
@@ -386,6 +418,75 @@ def main():
         "extras": extras,
     }
     print(json.dumps(out), flush=True)
+
+
+def mfma_ceiling(dev, props, launch_ms=100.0, timed=5):
+    """The matrix cores' sustained throughput on this GPU: the probe kernel
+    (attention_non_causal_amd/probe/mfma_ceiling.hip, two waves per SIMD, 16
+    independent MFMAs per loop turn, operands changing every instruction) for
+    bf16 32x32x16 and e4m3 32x32x64 on N(0,1) data and on zeros.  Each case:
+    0.3 s of launches to settle the clock, then `timed` launches of about
+    launch_ms each between events, then 1.5 s more while amd-smi samples the
+    shader clock."""
+    import ctypes
+    import numpy as np
+    import torch
+    from attention_non_causal_amd import build as libbuild
+    from attention_non_causal_amd import functional as F
+    if not os.path.exists(libbuild.PROBE_LIB_PATH):
+        raise SystemExit(f"{libbuild.PROBE_LIB_PATH} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(libbuild.PROBE_LIB_PATH)
+    lib.dit_probe_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.dit_probe_mfma_ceiling.restype = ctypes.c_int
+    n_blocks = 2 * props.multi_processor_count
+    out = torch.empty(n_blocks * 256, dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(42)
+    # operand data: 4096 words; bf16 N(0,1) bits, or e4m3 codes of N(0,1)
+    # values from the library's own quantiser (per-128-token-block scaled)
+    bf = torch.from_numpy(rng.standard_normal(8192).astype(np.float32)).to(torch.bfloat16)
+    src_bf16 = bf.view(torch.int16).to(dev).view(torch.int32).contiguous()
+    x = torch.from_numpy(rng.standard_normal(16384).astype(np.float32)).to(torch.bfloat16)
+    x8, _ = F.quantize_fp8(x.reshape(1, 128, 1, 128).to(dev))
+    src_fp8 = x8.reshape(-1).view(torch.int32).contiguous()
+    zeros = torch.zeros(4096, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"n_blocks": n_blocks, "waves_per_simd": 2}
+    for name, kind, src, flop in (("bf16_random", 0, src_bf16, 2 * 32 * 32 * 16),
+                                  ("bf16_zeros", 0, zeros, 2 * 32 * 32 * 16),
+                                  ("fp8_random", 1, src_fp8, 2 * 32 * 32 * 64),
+                                  ("fp8_zeros", 1, zeros, 2 * 32 * 32 * 64)):
+        def launch(iters):
+            st = lib.dit_probe_mfma_ceiling(src.data_ptr(), out.data_ptr(), n_blocks, iters,
+                                            kind, stream)
+            assert st == 0, f"probe launch failed: HIP status {st}"
+        # size the launch: time a short one after the clock has settled
+        settle(lambda: launch(2000), 0.3)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch(2000)
+        b.record()
+        torch.cuda.synchronize()
+        iters = max(1, int(2000 * launch_ms / a.elapsed_time(b)))
+        settle(lambda: launch(iters), 0.3)
+        evs = []
+        for _ in range(timed):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            launch(iters)
+            b.record()
+            torch.cuda.synchronize()
+            evs.append(a.elapsed_time(b))
+        ms = float(np.median(evs))
+        flops = n_blocks * 4 * 16 * iters * flop
+        mhz, n = sustained_clock(lambda: launch(iters // 10 or 1), 1.5)
+        res[name] = {"tflops": round(flops / ms / 1e9, 1), "launch_ms": round(ms, 3),
+                     "iters": iters, "sustained_sclk_mhz": mhz, "sclk_samples": n}
+        log(f"mfma ceiling {name}: {res[name]['tflops']} TFLOP/s ({ms:.3f} ms per launch of "
+            f"{iters} loop turns), shader clock {mhz} MHz")
+    return {"mfma_ceiling": res, "device": {"name": props.name,
+                                            "arch": getattr(props, "gcnArchName", None),
+                                            "cus": props.multi_processor_count}}
 
 
 def run_extras(dev, steps, warmup, settle_s):

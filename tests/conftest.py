@@ -26,4 +26,6 @@ def _oracle_built():
         libbuild.build()
     if not os.path.exists(_lib.DEBUG_LIB_PATH) and libbuild.hipcc():
         libbuild.build(debug_barriers=True)
+    if not os.path.exists(libbuild.PROBE_LIB_PATH) and libbuild.hipcc():
+        libbuild.build_probe()
     yield

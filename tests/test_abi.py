@@ -36,6 +36,19 @@ def test_library_exports_header_functions():
     assert set(names) <= exported
 
 
+def test_side_libraries_export_the_same_interface():
+    """The race-check build exports what the header declares, like the
+    library; the matrix-core probe exports its one entry."""
+    from attention_non_causal_amd import build as libbuild
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                             text=True, check=True).stdout
+        return {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(_lib.header_functions()) <= exported(_lib.DEBUG_LIB_PATH)
+    assert "dit_probe_mfma_ceiling" in exported(libbuild.PROBE_LIB_PATH)
+
+
 def test_version_and_status_strings():
     assert _lib.dit_version() == 10301
     texts = [_lib.dit_status_string(s) for s in range(9)]
