@@ -30,12 +30,12 @@
 //     same rounded weights (so O is a convex combination of the values and a
 //     single key returns its value), taken by one more MFMA per tile against
 //     an all-ones operand; LSE uses the sum of the unrounded weights.
-//   P^T operand: the S^T accumulator gives lane (n, half) keys 8q + 4*half +
-//     0..3 in register group q; after packing to e4m3 (4 keys per dword), one
-//     v_permlane32_swap per pair of groups makes lane half g hold keys
-//     16t + 8g + 0..7, matching the V operand read with ds_read_b64_tr_b8 (a
-//     16-lane group reads 8 key rows x 16 channels and lane i receives channel
-//     i of the 8 rows).
+//   P^T operand: the S^T accumulator gives lane (n, half) keys 32kb + 8q +
+//     4*half + 0..3 in register group q of block kb; packed to e4m3 in that
+//     order (4 keys per dword) it is the B operand as it stands: the V operand
+//     read with ds_read_b64_tr_b8 (a 16-lane group reads 8 key rows x 16
+//     channels and lane i receives channel i of the 8 rows) picks its rows so
+//     that the same keys land in the same k slots.
 //   Ping-pong between the two groups: a tile's work is a matrix phase (P.V of
 //     the tile before, its rounded-weight sum, K Q^T of this tile: 9 MFMAs)
 //     and a vector phase (the softmax of this tile).  Each SIMD holds one wave
@@ -85,16 +85,17 @@ struct FwdFp8Cfg {
     static constexpr int kScaleBlock = 128;               // tokens per block scale
 };
 
-// Chunk slot of chunk c in row r.
+// Chunk slot of chunk c in row r: a permutation of the row's chunks chosen so
+// that the 16-row K operand reads and the 8-row V transpose reads (the rows
+// that the V addresses below pick) are free of bank conflicts.
 template <int D>
 __device__ __forceinline__ int fp8_slot(int r, int c)
 {
     if constexpr (D == 128) {
         const int u = (r >> 1) & 7;
-        return c ^ (((u & 3) << 1) | (u >> 2));
+        return c ^ (((u & 1) << 1) | ((u >> 1) & 1) | (u & 4));
     } else {
-        const int u = (r >> 2) & 3;
-        return c ^ (((u & 1) << 1) | (u >> 1));
+        return c ^ ((r >> 2) & 3);
     }
 }
 
@@ -399,16 +400,14 @@ struct FwdFp8Tile {
         const float inv_fk = __builtin_amdgcn_rcpf(vmant * Cfg::kPScale);
         l_run += lsum * inv_fk;
 
-        // regroup so lane half g holds keys 16t + 8g + 0..7 in dwords (2t, 2t+1)
+        // P''^T in the k order of the P.V instruction as packed: dword 4 kb + q
+        // holds keys 32 kb + 8 q + 4 hh + 0..3, which the V^T reads put in the
+        // same k slots (see the V addresses in the kernel)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(
-                    (int)pw[kb][2 * t2], (int)pw[kb][2 * t2 + 1], false, false);
-                pf[2 * (2 * kb + t2)] = sw[0];
-                pf[2 * (2 * kb + t2) + 1] = sw[1];
-            }
+            for (int q = 0; q < 4; ++q)
+                pf[4 * kb + q] = (int)pw[kb][q];
         p_vexp = vexp;
         rs_inv = inv_fk;
     }
@@ -546,16 +545,21 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 1) void fwd_fp8_kernel(
     }
 
     // K operand (A of S^T), step s: row n (+32 for the second block), bytes
-    // 64s + 32hh .. +31 (two chunks).  V transpose reads, block mb: lane group
-    // (hh, g2 = (lane/16)%2) reads rows 8hh + (lane%16)/2 (+16t) at channels
-    // 32mb + 16g2 + 8(lane%2) .. +7.
+    // 64s + 32hh .. +31 (two chunks).  V transpose reads, block mb: lane pair p
+    // = (lane%16)/2 of lane group (hh, g2 = (lane/16)%2) reads row
+    // 8(p/4) + 4hh + p%4 (+16t) at channels 32mb + 16g2 + 8(lane%2) .. +7, so
+    // byte p of read t holds key 16t + 8(p/4) + 4hh + p%4: k slot 32hh + 8t +
+    // p of the MFMA, the slot the S^T accumulator layout gives that key's
+    // weight when packed in register order (valu_phase), so P^T needs no
+    // exchange between lanes.
 #pragma unroll
     for (int s = 0; s < Cfg::kKSteps; ++s)
 #pragma unroll
         for (int e = 0; e < 2; ++e)
             st.k_addr[s][e] = fp8_lds_byte<D>(n, 64 * s + 32 * hh + 16 * e);
     {
-        const int vr = 8 * hh + ((lane & 15) >> 1);
+        const int vp = (lane & 15) >> 1;
+        const int vr = 8 * (vp >> 2) + 4 * hh + (vp & 3);
         const int vc = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
