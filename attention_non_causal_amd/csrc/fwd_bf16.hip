@@ -896,13 +896,13 @@ hipError_t launch_fwd_bf16_d(const FwdArgs& a, const FwdSplit& sp, hipStream_t s
 
 FwdSplit plan_fwd_bf16_split(int B, int H, int Sq, int Skv, int d, int n_cu)
 {
-    return d == 64 ? plan_d<64>(B, H, Sq, Skv, n_cu) : plan_d<128>(B, H, Sq, Skv, n_cu);
+    return d == 64 ? plan_d<64>(B, H, Sq, Skv, n_cu) : plan_fwd_bf16_d128_split(B, H, Sq, Skv, n_cu);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdSplit& split, hipStream_t stream)
 {
     return a.d == 64 ? launch_fwd_bf16_d<64>(a, split, stream)
-                     : launch_fwd_bf16_d<128>(a, split, stream);
+                     : launch_fwd_bf16_d128(a, split, stream);
 }
 
 }  // namespace dit

@@ -57,6 +57,10 @@ hipError_t launch_split_merge(const FwdArgs& a, const FwdSplit& sp, int rows, in
                               hipStream_t stream);
 
 FwdSplit plan_fwd_bf16_split(int B, int H, int Sq, int Skv, int d, int n_cu);
+// head size 128 (fwd_bf16_d128.hip; plan_fwd_bf16_split and launch_fwd_bf16
+// dispatch to these)
+FwdSplit plan_fwd_bf16_d128_split(int B, int H, int Sq, int Skv, int n_cu);
+hipError_t launch_fwd_bf16_d128(const FwdArgs& a, const FwdSplit& split, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdSplit& split, hipStream_t stream);
 FwdSplit plan_fwd_fp8_split(int B, int H, int Sq, int Skv, int d, int n_cu);
 hipError_t launch_fwd_fp8(const FwdArgs& a, const FwdSplit& split, hipStream_t stream);

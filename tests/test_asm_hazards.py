@@ -28,9 +28,12 @@ import pytest
 
 from attention_non_causal_amd import build as libbuild
 
-SOURCES = ("fwd_bf16.hip", "fwd_fp8.hip")
+SOURCES = ("fwd_bf16.hip", "fwd_bf16_d128.hip", "fwd_fp8.hip")
+# forward kernels per source (template instantiations)
+N_KERNELS = {"fwd_bf16.hip": 1, "fwd_bf16_d128.hip": 1, "fwd_fp8.hip": 2}
 VALU_TO_MFMA = 2
 MFMA_TO_VALU = 18      # 8-pass v_mfma_f32_32x32x16_bf16 (needs 11)
+MFMA4_TO_VALU = 11     # 4-pass v_mfma_f32_16x16x32_bf16 (needs 7)
 MFMA16_TO_VALU = 19    # 16-pass v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3)
 MFMA8_SCALE_TO_VALU = 11  # 8-pass v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3)
 
@@ -64,7 +67,7 @@ def _kernels(text):
     out, cur, name = [], None, None
     for line in text.splitlines():
         s = line.strip()
-        if re.match(r"^_Z\S*fwd_(bf16|fp8)_kernel\S*:", s):
+        if re.match(r"^_Z\S*fwd_(bf16|bf16_d128|fp8)_kernel\S*:", s):
             name, cur = s[:-1], []
             continue
         if cur is None:
@@ -93,6 +96,8 @@ def _cost(ins):
 def _after(op):
     if op.startswith("v_mfma_scale_f32_16x16x128"):
         return MFMA8_SCALE_TO_VALU
+    if op.startswith("v_mfma_f32_16x16x32"):
+        return MFMA4_TO_VALU
     return MFMA16_TO_VALU if op.startswith("v_mfma_scale") else MFMA_TO_VALU
 
 
@@ -134,7 +139,7 @@ def _check(body):
 @pytest.mark.parametrize("name", SOURCES)
 def test_no_unprotected_mfma_hazards(name):
     kernels = _kernels(_asm(name))
-    assert len(kernels) == 2, [k for k, _ in kernels]
+    assert len(kernels) == N_KERNELS[name], [k for k, _ in kernels]
     problems = []
     for name, body in kernels:
         n_mfma = sum(1 for ins in body if ins[0].startswith("v_mfma"))
@@ -162,6 +167,6 @@ def test_debug_barrier_build_adds_barriers(name):
     def barriers(text):
         return {k: sum(1 for ins in body if ins[0] == "s_barrier") for k, body in _kernels(text)}
     normal, debug = barriers(_asm(name)), barriers(_asm(name, ("-DDIT_DEBUG_BARRIERS",)))
-    assert normal.keys() == debug.keys() and len(normal) == 2
+    assert normal.keys() == debug.keys() and len(normal) == N_KERNELS[name]
     for k in normal:
         assert debug[k] > normal[k], (k, normal[k], debug[k])
