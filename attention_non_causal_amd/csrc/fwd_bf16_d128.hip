@@ -76,7 +76,7 @@ struct CfgD128 {
     static constexpr int kHalf = kRing / 2;               // iterations per barrier
     static constexpr int kSlots = 4 * kCB;                // slots per iteration
     static constexpr int kCopySlotV = 1;                  // slots that issue the copies
-    static constexpr int kCopySlotK = 17;
+    static constexpr int kCopySlotK = 5;
     static constexpr int kBarrierSlot = 29;               // see slot()
     // Bound on one lane's sum of weights of one tile and query (16 weights),
     // which keeps every weight <= 2^32: O and the sums cannot overflow for
@@ -97,14 +97,18 @@ __device__ __forceinline__ int k_lds_byte(int r, int col)
 }
 
 // Keep a vector-ALU result where it is computed (see the slot program).
-__device__ __forceinline__ void pin(float& x)
+__device__ __forceinline__ void pin(uint32_t& x)
 {
     asm volatile("" : "+v"(x));
 }
 
-__device__ __forceinline__ void pin(uint32_t& x)
+// Have x computed before this point, without redefining it: the compiler
+// takes every register an asm statement writes to need a forwarding wait
+// state before a vector instruction reads it, so a pin (above) right before
+// such a read costs an s_nop.
+__device__ __forceinline__ void use(float x)
 {
-    asm volatile("" : "+v"(x));
+    asm volatile("" ::"v"(x));
 }
 
 // The matrix instructions of the tile loop are asm statements, so that their
@@ -304,9 +308,11 @@ struct TileD128 {
     __device__ __forceinline__ void softmax_part()
     {
         constexpr int b = I / 4, qb = b % 2, i = I % 4;
-        pin(m_used[qb]);
-        float e = exp2_fast(__builtin_fmaf(sacc[b][i], scale_log2, -m_used[qb]));
-        pin(e);
+        use(m_used[qb]);
+        const float x = __builtin_fmaf(sacc[b][i], scale_log2, -m_used[qb]);
+        use(x);
+        const float e = exp2_fast(x);
+        use(e);
         sacc[b][i] = e;
         if constexpr (I > 0)
             fold<P, I - 1>();
@@ -321,7 +327,7 @@ struct TileD128 {
         constexpr int b = J / 4, kb = b / 2, qb = b % 2, i = J % 4;
         const float e = sacc[b][i];
         lsum[qb] = (J == 4 * qb) ? e : lsum[qb] + e;
-        pin(lsum[qb]);
+        use(lsum[qb]);
         if constexpr (i % 2 == 1) {
             uint32_t pk = pack_bf16x2(sacc[b][i - 1], e);
             pin(pk);
