@@ -84,11 +84,16 @@ struct CfgD128 {
     static constexpr float kWeightSumLimit = 0x1p32f;
 };
 
-// Chunk slot of chunk c in K row r (a bit permutation of r's low 4 bits XORed
-// in): 16 consecutive rows read at one chunk hit 16 distinct chunk slots.
+// Chunk slot of chunk c in K row r: c XOR a permutation of r's low 4 bits
+// (row bits 0, 1, 2, 3 to slot bits 0, 2, 1, 3), so 16 consecutive rows at one
+// chunk sit in 16 distinct slots.  A K operand read (lane l: row l % 16, plus
+// 16 per key block, chunk 4s + l / 16) is then free of bank conflicts; among
+// the XOR permutations of this family some are and some are not, as measured
+// with SQ_LDS_BANK_CONFLICT on the bare read pattern (row bits to slot bits
+// 2, 3, 0, 1, for one, cost 4 extra cycles per read).
 __device__ __forceinline__ int k_slot(int r, int c)
 {
-    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    return c ^ ((r & 9) | ((r & 2) << 1) | ((r & 4) >> 1));
 }
 
 __device__ __forceinline__ int k_lds_byte(int r, int col)

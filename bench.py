@@ -32,7 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0
 # rocprofv3 summary of the dominant kernel and the sources it was taken from;
 # its traffic figure is reported only while those sources are unchanged
 PROFILE = os.path.join(ROOT, "profiles", "fwd_bf16_d128_flux.md")
-PROFILE_SOURCES = ("attention_non_causal_amd/csrc/fwd_bf16.hip",
+PROFILE_SOURCES = ("attention_non_causal_amd/csrc/fwd_bf16_d128.hip",
                    "attention_non_causal_amd/csrc/common.hpp")
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
@@ -315,7 +315,9 @@ def main():
                          "shader clock has settled (0: only the warmup calls)")
     ap.add_argument("--clock-seconds", type=float, default=1.5,
                     help="seconds of back-to-back steps after the timed ones while amd-smi "
-                         "samples the shader clock (0: skip)")
+                         "samples the shader clock (0: skip, and run no amd-smi at all: "
+                         "under rocprofv3 --pmc the GPU is initialised before the program "
+                         "starts, and amd-smi re-executes itself)")
     ap.add_argument("--fp8-rows", type=int, default=64,
                     help="query rows of the fp8 workloads compared with the oracle in the "
                          "cpu_baseline leg")
@@ -402,13 +404,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(), "traffic_unit": "bytes/launch",
                      "algorithmic_bytes": W.algorithmic_bytes,
-                     "kernel": "fwd_bf16_kernel<128> (+ split_merge_kernel<128>, a few us)",
+                     "kernel": "fwd_bf16_d128_kernel (+ split_merge_kernel<128>, a few us)",
                      "kernel_ms": round(kern_ms, 4),
                      "kernel_ms_median": round(float(np.median(evs)), 4),
                      "kernel_ms_min": round(float(min(evs)), 4),
                      "first_launch_ms": round(cold_ms, 4)},
         "cpu_baseline": cpu,
-        "device": {"name": _smi_market_name() or props.name, "torch_name": props.name,
+        "device": {"name": (_smi_market_name() if args.clock_seconds > 0 else None) or props.name,
+                   "torch_name": props.name,
                    "arch": getattr(props, "gcnArchName", None),
                    "cus": props.multi_processor_count,
                    "sustained_sclk_mhz": clock_mhz, "sclk_samples": clock_n,
@@ -526,7 +529,9 @@ def run_extras(dev, steps, warmup, settle_s):
     wall, evs = time_launches(
         lambda: F.ring_share_attention(q, k, v, W.n_chunks, W.scale, parts=parts, out=o, lse=lse),
         steps, warmup, settle_s)
-    ms = float(np.mean(evs))
+    # medians: one slow call (a clock dip, a page of the inputs faulting in)
+    # moves a mean of a handful of calls by several percent
+    ms = float(np.median(evs))
     mms = time_batched(lambda: F.merge(parts[0], parts[1], out=o, lse=lse), 4 * steps, warmup,
                        settle_s)
     merge_bytes = W.n_chunks * (W.Sq * W.H * W.d * 2 + W.H * W.Sq * 4) + W.Sq * W.H * W.d * 2 \
@@ -539,7 +544,7 @@ def run_extras(dev, steps, warmup, settle_s):
         lambda: F.ring_share_attention_acc(q, k, v, W.n_chunks, W.scale, out=o, lse=lse,
                                            workspace=aws),
         steps, warmup, settle_s)
-    ams = float(np.mean(aevs))
+    ams = float(np.median(aevs))
     res["wan_ring"] = {"total_ms": round(ms, 4), "tflops": round(W.flops / ms / 1e9, 1),
                        "merge_ms": round(mms, 4),
                        "merge_GBs": round(merge_bytes / mms / 1e6, 1),
@@ -580,9 +585,9 @@ def run_extras(dev, steps, warmup, settle_s):
     res["quant_fp8"] = {"kernel_ms": round(qms, 4), "GBs": round(qbytes / qms / 1e6, 1)}
     log(f"extra quant_fp8 (one tensor): {qms:.4f} ms = {res['quant_fp8']['GBs']} GB/s")
     _, aevs = time_launches(attn_fp8, steps, warmup, settle_s)
-    ams = float(np.mean(aevs))
+    ams = float(np.median(aevs))
     _, levs = time_launches(lambda: (quant_all(), attn_fp8()), steps, warmup, settle_s)
-    lms = float(np.mean(levs))
+    lms = float(np.median(levs))
     res["flux_fp8"] = {"kernel_ms": round(ams, 4), "tflops": round(W.flops / ams / 1e9, 1),
                        "pct_of_fp8_peak": round(100 * W.flops / ams / 1e9 / PEAK_FP8_TFLOPS, 2),
                        "layer_ms_with_quant": round(lms, 4),
