@@ -1,5 +1,7 @@
 // fwd_bf16.hip -- non-causal attention forward pass (O + LSE) in bf16 with
-// fp32 accumulation, for gfx950 (CDNA4) MFMA.
+// fp32 accumulation, for gfx950 (CDNA4) MFMA: head size 64.  (Head size 128
+// runs the kernel of fwd_bf16_d128.hip, built on 16x16x32 accumulate chains;
+// this one is built on v_mfma_f32_32x32x16_bf16.)
 //
 // What is computed: per (batch, head), O = softmax(scale * Q K^T) V and
 // LSE = ln sum_j exp(scale * q . k_j) -- the whole-sequence, cache-free
@@ -10,11 +12,10 @@
 // (online softmax).
 //
 // Work decomposition
-//   Each wave owns 32 query rows of one (batch, head).  d = 128: a workgroup
-//   of 8 waves (256 rows), one per CU -- every K/V tile copied into LDS then
-//   serves 256 rows, which halves copy traffic against 4-wave workgroups;
-//   d = 64: 4 waves (128 rows), two workgroups per CU.  Either way each SIMD
-//   runs two waves.  Keys stream through LDS in tiles of 64.  Copies go
+//   Each wave owns 32 query rows of one (batch, head); a workgroup holds 4
+//   waves (128 rows), and the launch bound asks for two workgroups per CU
+//   (the registers and LDS leave room for a third, which the hardware
+//   places).  Keys stream through LDS in tiles of 64.  Copies go
 //   global -> LDS by buffer_load_dwordx4 ... lds (no VGPR staging); each
 //   lane's buffer offset within a tile is fixed for the whole kernel and the
 //   tile's start is a scalar offset.  Rows past the last key lie outside the
@@ -30,16 +31,15 @@
 //       to k slots, so no register shuffle is needed.
 //   Software pipeline: iteration j runs the P V product of tile j-1, the K Q^T
 //   product of tile j+1 and the softmax of tile j.  The three are independent,
-//   so the 32 (d = 128) matrix instructions of an iteration interleave the two
+//   so the 16 matrix instructions of an iteration interleave the two
 //   products (per 16-key step: its P V instructions, then as many K Q^T ones),
 //   and the softmax's vector instructions are spread over the same slots: the
 //   vector ALU works in the shadow of the matrix core instead of after it.
 //   The slots are fenced (sched_barrier) so the compiler keeps that order.
 //   LDS operands are read several slots ahead: V^T fragments one 16-key step
-//   ahead, K operands during the group of slots before (d = 64: the last
-//   group's; the others kMB slots ahead), and the first V^T fragments of
-//   iteration j+1 during the last group of iteration j, so that no iteration
-//   starts by waiting on LDS.
+//   ahead, K operands kMB slots ahead (the last group's during the group
+//   before), and the first V^T fragments of iteration j+1 during the last
+//   group of iteration j, so that no iteration starts by waiting on LDS.
 //   Softmax in the log2 domain: scale*log2(e) is folded into one FMA before
 //   v_exp_f32.  The weights of a whole pass over the keys are taken against one
 //   reference maximum (the first tile's row maximum): the final O / sum and LSE
@@ -48,8 +48,8 @@
 //   so far above the reference that a lane's weight sum for a tile passes
 //   2^32, the workgroup computes the exact row maxima of its key range and
 //   makes the pass again (see the kernel).
-//   LDS: a ring of K and V tile buffers (four slots each for d = 128, two for
-//   d = 64), each its own LDS object.  Iteration j reads K(j+1), V(j-1) from
+//   LDS: a ring of K and V tile buffers (two slots each; with two or three
+//   workgroups per CU a deeper ring was slower), each its own LDS object.  Iteration j reads K(j+1), V(j-1) from
 //   slot j while the copies of the tiles that iteration j + kRing/2 reads go
 //   into slot j + kRing/2, last read by iteration j - kRing/2: one barrier
 //   per kRing/2 iterations.  It sits before the last group of K Q^T
@@ -75,10 +75,9 @@ namespace {
 
 template <int D>
 struct FwdBf16Cfg {
-    // d = 128: one workgroup of 8 waves per CU, so 256 query rows share every
-    // K/V tile copied into LDS; d = 64: two workgroups of 4 waves per CU.
-    static constexpr int kWaves = D == 128 ? 8 : 4;
-    static constexpr int kWgPerCu = D == 128 ? 1 : 2;
+    static_assert(D == 64, "head size 128 runs fwd_bf16_d128.hip");
+    static constexpr int kWaves = 4;
+    static constexpr int kWgPerCu = 2;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBr = 32 * kWaves;                // query rows per workgroup
     static constexpr int kBc = 64;                         // keys per tile
@@ -88,21 +87,8 @@ struct FwdBf16Cfg {
     static constexpr int kLoads = kTileBytes / (16 * kThreads);  // 16-B loads per thread
     static constexpr int kLoadRows = 16 * kThreads / kRowBytes;   // rows one copy covers
     static constexpr int kMB = D / 32;                     // 32-channel output blocks
-    // Slots after whose matrix instruction an iteration issues its V and K
-    // copies (-1: before the first); d = 128 keeps them out of the burst of
-    // LDS reads that follows the barrier.
-    static constexpr int kCopySlotV = D == 128 ? 0 : -1;
-    static constexpr int kCopySlotK = D == 128 ? 8 : -1;
     static constexpr int kVBlockBytes = kBc * 64;          // V tile: one 32-channel block
-    // K and V tile buffers each (ring slots).  d = 128: four, so that one
-    // barrier serves two iterations; d = 64: two (with two workgroups per CU
-    // the deeper ring was slower).
-    static constexpr int kRing = D == 128 ? 4 : 2;
-    // Softmax sums and bf16 pairs one slot after the weights (see softmax_part).
-    static constexpr bool kFoldLater = D == 128;
-    // K operands read a whole group of slots ahead (see slot()).  Both were
-    // faster for d = 128 and slower for d = 64.
-    static constexpr bool kKAhead = D == 128;
+    static constexpr int kRing = 2;                        // K and V tile buffers each
     // Bound on one lane's sum of weights of one tile (32 weights), which keeps
     // every weight <= 2^32: O and the sums cannot overflow for |V| < 2^80.
     static constexpr float kWeightSumLimit = 0x1p32f;
@@ -112,12 +98,8 @@ struct FwdBf16Cfg {
 template <int D>
 __device__ __forceinline__ int swz_slot(int r, int c)
 {
-    if constexpr (D == 128) {
-        return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
-    } else {
-        const int u = (r >> 1) & 7;
-        return c ^ (((u & 1) << 2) | (u >> 1));
-    }
+    const int u = (r >> 1) & 7;
+    return c ^ (((u & 1) << 2) | (u >> 1));
 }
 
 template <int D>
@@ -216,12 +198,11 @@ struct FwdBf16Tile {
     u32x4 pf[2][4];          // [parity][16-key step]: P^T of a tile
     u32x2 vf[kVReads];       // V^T fragments of one 16-key step
     u32x4 kf[kMB];           // K fragments of one group of K Q^T slots
-    uint32_t pw[2];          // bf16 pairs of the even group of a 16-key step (d = 64)
+    uint32_t pw[2];          // bf16 pairs of the even group of a 16-key step
     float lsum;              // sum of this lane's weights of the current tile
     float lsum_max;          // largest lsum of the pass (checked against kWeightSumLimit)
     float m_used;  // reference maximum (scale*log2(e) units) of the weights, fixed per pass
     float l_run;   // running sum over this lane's half of the keys
-    int copy_kt;   // tile of the current iteration (for copies issued in its slots)
 
     // Copy tile kt of K (to K ring slot KB) and/or of V (to V slot VB) into LDS;
     // a negative buffer index skips that tensor.  Rows past the last key lie
@@ -272,16 +253,6 @@ struct FwdBf16Tile {
         kf[Q % kMB] = ld_k<KB>(Q / 2, Q % 2);
     }
 
-    // K operands 0 .. kMB-2 of the first group of K Q^T slots from slot KB.
-    template <int KB, int J = 0>
-    __device__ __forceinline__ void read_ks()
-    {
-        if constexpr (J < kMB - 1) {
-            read_k<KB, J>();
-            read_ks<KB, J + 1>();
-        }
-    }
-
     // Transpose read E (block E/2, half E%2) of 16-key step T from V slot VB:
     // this lane's address in V slot 0 plus a constant, written so that the
     // constant (the slot's distance from slot 0, the block, the keys) folds
@@ -325,10 +296,8 @@ struct FwdBf16Tile {
     // the kernel), so a tile needs no maximum of its own.  Score w is register
     // w%16 of 32-key block w/16; slot I computes weights kW*I .. kW*I + kW-1
     // in place (block 1's from slot 16/kW >= 8 on, well after its last K Q^T
-    // step).  Their sum and bf16 pairs:
-    //   d = 128 (kFoldLater): one slot later (fold), so that no instruction
-    //     waits on an exponential of its own slot;
-    //   d = 64: per group of 4 weights, in the group's last slot (faster there).
+    // step).  Their sum and bf16 pairs come per group of 4 weights, in the
+    // group's last slot.
     static constexpr int kW = 32 / kSlots;  // weights per slot
 
     template <int P, int I>
@@ -343,10 +312,7 @@ struct FwdBf16Tile {
             pin(e);
             sacc[P][w / 16][w % 16] = e;
         }
-        if constexpr (Cfg::kFoldLater) {
-            if constexpr (I > 0)
-                fold<P, I - 1>();
-        } else if constexpr ((kW * (I + 1)) % 4 == 0) {
+        if constexpr ((kW * (I + 1)) % 4 == 0) {
             // group of weights w0 .. w0+3 complete: its sum, and its two bf16
             // pairs (words 2(G%2), 2(G%2)+1 of the P^T fragment of step t)
             constexpr int w0 = kW * (I + 1) - 4, G = w0 / 4, kb = w0 / 16, r0 = w0 % 16;
@@ -365,24 +331,6 @@ struct FwdBf16Tile {
                            pack_bf16x2(s[r0 + 2], s[r0 + 3])};
                 pin(v);
                 pf[P][t] = v;
-            }
-        }
-    }
-
-    // The weights of slot J into lsum and into P^T: the fragment of 16-key
-    // step t holds registers 8(t%2) .. 8(t%2)+7 of block t/2 as bf16 pairs.
-    template <int P, int J>
-    __device__ __forceinline__ void fold()
-    {
-#pragma unroll
-        for (int w = kW * J; w < kW * (J + 1); ++w) {
-            const float e = sacc[P][w / 16][w % 16];
-            lsum = w == 0 ? e : lsum + e;
-            pin(lsum);
-            if (w % 2 == 1) {
-                uint32_t pk = pack_bf16x2(sacc[P][w / 16][w % 16 - 1], e);
-                pin(pk);
-                pf[P][w / 8][(w % 8) / 2] = pk;
             }
         }
     }
@@ -441,13 +389,12 @@ struct FwdBf16Tile {
     //   last kMB:  S^T += K Q^T for the next tile (K from slot R), K Q^T
     //              instructions kMB t .. kMB t + kMB-1 (k step q/2, 32-key
     //              block q%2), pairs with the same B operand.
-    // (Grouping instructions that share an operand was +3.5% for d = 64 and
-    // neutral for d = 128 against alternating the two products.)
+    // (Grouping instructions that share an operand was +3.5% against
+    // alternating the two products.)
     template <int R, int I>
     __device__ __forceinline__ void slot()
     {
         constexpr int P = R % 2;
-        constexpr int W = (R + kHalf) % Cfg::kRing;  // ring slot this iteration's copies fill
         constexpr int t = I / (2 * kMB), i = I % (2 * kMB);
         if constexpr (I == kSlots - kMB) {
             // The group's barrier: every wave's copies so far have landed (so
@@ -468,35 +415,21 @@ struct FwdBf16Tile {
             constexpr int mb = i;
             mfma_o(oacc[mb], u32x4{vf[2 * mb][0], vf[2 * mb][1], vf[2 * mb + 1][0], vf[2 * mb + 1][1]},
                    pf[P ^ 1][t]);
-            if constexpr (Cfg::kKAhead) {
-                // K operand of this group's last K Q^T instruction (the others
-                // were read during the group before)
-                if constexpr (i == 0)
-                    read_k<R, kMB * t + kMB - 1>();
-            } else {
-                // K operand of this group's K Q^T instruction i, kMB slots
-                // ahead (last group: read in the group before)
-                if constexpr (t < 3)
-                    read_k<R, kMB * t + i>();
-                if constexpr (t == 3 && i == 0)
-                    read_k<R, kMB * 3 + kMB - 1>();
-            }
+            // K operand of this group's K Q^T instruction i, kMB slots ahead
+            // (last group: read in the group before)
+            if constexpr (t < 3)
+                read_k<R, kMB * t + i>();
+            if constexpr (t == 3 && i == 0)
+                read_k<R, kMB * 3 + kMB - 1>();
         } else {
             constexpr int v = kMB * t + i - kMB, s = v / 2, kb = v % 2;
             if constexpr (s == 0)
                 mfma_s0(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
             else
                 mfma_s(sacc[P ^ 1][kb], kf[v % kMB], qf[s]);
-            // K operands of the next group (kKAhead; the last group: of the
-            // next iteration's first group, from its ring slot), else of the
-            // last group only, one slot after their registers' last use
-            if constexpr (Cfg::kKAhead && i > kMB) {
-                if constexpr (t < 3)
-                    read_k<R, kMB * (t + 1) + (i - kMB - 1)>();
-                else
-                    read_k<(R + 1) % Cfg::kRing, i - kMB - 1>();
-            }
-            if constexpr (!Cfg::kKAhead && t == 2 && i > kMB)
+            // K operands of the last group, one slot after their registers'
+            // last use
+            if constexpr (t == 2 && i > kMB)
                 read_k<R, kMB * 3 + (i - kMB - 1)>();
         }
         // V^T fragments 2mb, 2mb+1 of step t+1, one slot after step t's block
@@ -507,10 +440,6 @@ struct FwdBf16Tile {
             read_v<R, t + 1, 2 * mb + 1>();
         }
         softmax_part<P, I>();
-        if constexpr (I == Cfg::kCopySlotV)
-            copy_tile<-1, W>(copy_kt + kHalf - 1);
-        if constexpr (I == Cfg::kCopySlotK)
-            copy_tile<W, -1>(copy_kt + kHalf + 1);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -524,8 +453,7 @@ struct FwdBf16Tile {
     }
 
     // The P V product of the last tile alone (after an even number of
-    // iterations: P^T in pf[1], V in ring slot 0 or, for four slots, 2, as
-    // vb says).
+    // iterations: P^T in pf[1], V in ring slot 0, which vb is).
     __device__ __forceinline__ void drain(const uint8_t* vb)
     {
         constexpr int P = 0;
@@ -554,11 +482,8 @@ struct FwdBf16Tile {
     {
         constexpr int P = R % 2;
         constexpr int W = (R + kHalf) % Cfg::kRing;
-        copy_kt = kt;
-        if constexpr (Cfg::kCopySlotV < 0)
-            copy_tile<-1, W>(kt + kHalf - 1);
-        if constexpr (Cfg::kCopySlotK < 0)
-            copy_tile<W, -1>(kt + kHalf + 1);
+        copy_tile<-1, W>(kt + kHalf - 1);
+        copy_tile<W, -1>(kt + kHalf + 1);
         const int key0 = kt * kBc;
         if (key0 + kBc > key_end)
             mask_tile<P>(key0);
@@ -567,8 +492,6 @@ struct FwdBf16Tile {
         pin(v_reg);
         __builtin_amdgcn_sched_barrier(0);
         slots<R, 0>();
-        if constexpr (Cfg::kFoldLater)
-            fold<P, kSlots - 1>();
         l_run += lsum;
         lsum_max = fmaxf(lsum_max, lsum);
         debug_sync();
@@ -594,16 +517,10 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     constexpr int kRow = Cfg::kRowBytes;
     constexpr int kRing = Cfg::kRing;
     constexpr int kHalf = kRing / 2;
-    // (slots 2 and 3 are referenced only with four slots; unreferenced LDS
-    // objects take no space)
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[Cfg::kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[Cfg::kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds3[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[Cfg::kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[Cfg::kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[Cfg::kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds3[Cfg::kTileBytes];
     __shared__ int wave_over[Cfg::kWaves];
 
     const int tid = threadIdx.x;
@@ -636,12 +553,6 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     st.kobj[1] = k_lds1;
     st.vobj[0] = v_lds0;
     st.vobj[1] = v_lds1;
-    if constexpr (kRing == 4) {
-        st.kobj[2] = k_lds2;
-        st.kobj[3] = k_lds3;
-        st.vobj[2] = v_lds2;
-        st.vobj[3] = v_lds3;
-    }
     st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     st.hh = hh;
     st.key_end = min(kt1 * Cfg::kBc, Skv);
@@ -673,16 +584,12 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
     }
     // A pass starts with what its first kHalf iterations read: K(kt0) in the
     // last ring slot (the prologue's K Q^T), K(kt0+1) .. K(kt0+kHalf) in
-    // slots 0 .. kHalf-1, V(kt0) in slot 1 when four slots, and V(kt0) in
-    // slot 0, where the first iteration's P V (with P = 0) reads finite
-    // values.  (The first pass's copies overlap the Q loads.)
+    // slots 0 .. kHalf-1, and V(kt0) in slot 0, where the first iteration's
+    // P V (with P = 0) reads finite values.  (The first pass's copies overlap
+    // the Q loads.)
     auto pass_copies = [&]() {
         st.template copy_tile<kRing - 1, -1>(kt0);
         st.template copy_tile<0, -1>(kt0 + 1);
-        if constexpr (kRing == 4) {
-            st.template copy_tile<1, -1>(kt0 + 2);
-            st.template copy_tile<-1, 1>(kt0);
-        }
         st.template copy_tile<-1, 0>(kt0);
     };
     pass_copies();
@@ -752,9 +659,6 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
 #pragma unroll
         for (int e = 0; e < 2 * kMB; ++e)
             st.vf[e] = st.template ld_v<0>(0, e);
-        // and (kKAhead) the K operands of its first group, but the last
-        if constexpr (Cfg::kKAhead)
-            st.template read_ks<0>();
 
         // One iteration per tile of the range, unrolled over the ring slots
         // (the slot indices are compile-time), then the last tile's P V: by
@@ -763,23 +667,9 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
         const int n_it = kt1 - kt0;
         const int n_pad = (n_it + 1) & ~1;
         int i = 0;
-        if constexpr (kRing == 4) {
-            for (; i + 4 <= n_pad; i += 4) {
-                st.template iteration<0>(kt0 + i);
-                st.template iteration<1>(kt0 + i + 1);
-                st.template iteration<2>(kt0 + i + 2);
-                st.template iteration<3>(kt0 + i + 3);
-            }
-            if (i < n_pad) {
-                st.template iteration<0>(kt0 + i);
-                st.template iteration<1>(kt0 + i + 1);
-                i += 2;
-            }
-        } else {
-            for (; i < n_pad; i += 2) {
-                st.template iteration<0>(kt0 + i);
-                st.template iteration<1>(kt0 + i + 1);
-            }
+        for (; i < n_pad; i += 2) {
+            st.template iteration<0>(kt0 + i);
+            st.template iteration<1>(kt0 + i + 1);
         }
         // the last iteration's K Q^T result (of a tile past the range) is
         // dead: hold its registers until that matrix instruction is done
@@ -787,7 +677,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, FwdBf16Cfg<D>::kWgPerCu) v
         for (int kb = 0; kb < 2; ++kb)
             vgpr_wait(st.sacc[0][kb]);
         if (i == n_it)
-            st.drain(i % kRing == 0 ? st.vobj[0] : st.vobj[kRing - 2]);
+            st.drain(st.vobj[0]);
 
         if (lane == 0)
             wave_over[st.wave] = __builtin_amdgcn_ballot_w64(st.lsum_max > Cfg::kWeightSumLimit) != 0;
