@@ -342,7 +342,7 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     if args.mfma_ceiling:
-        print(json.dumps(mfma_ceiling(dev, props)), flush=True)
+        print(json.dumps(mfma_ceiling(dev, props, clock_s=args.clock_seconds)), flush=True)
         return
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -423,14 +423,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def mfma_ceiling(dev, props, launch_ms=100.0, timed=5):
+def mfma_ceiling(dev, props, launch_ms=100.0, timed=5, clock_s=1.5):
     """The matrix cores' sustained throughput on this GPU: the probe kernel
     (attention_non_causal_amd/probe/mfma_ceiling.hip, two waves per SIMD, 16
-    independent MFMAs per loop turn, operands changing every instruction) for
-    bf16 32x32x16 and e4m3 32x32x64 on N(0,1) data and on zeros.  Each case:
+    MFMAs per loop turn, operands changing every instruction) for bf16
+    32x32x16 and e4m3 32x32x64 on N(0,1) data and on zeros, and bf16 16x16x32
+    on N(0,1) data, in rotation and in chains of four dependent instructions.  Each case:
     0.3 s of launches to settle the clock, then `timed` launches of about
-    launch_ms each between events, then 1.5 s more while amd-smi samples the
-    shader clock."""
+    launch_ms each between events, then clock_s seconds more while amd-smi
+    samples the shader clock (0: none)."""
     import ctypes
     import numpy as np
     import torch
@@ -457,6 +458,8 @@ def mfma_ceiling(dev, props, launch_ms=100.0, timed=5):
     res = {"n_blocks": n_blocks, "waves_per_simd": 2}
     for name, kind, src, flop in (("bf16_random", 0, src_bf16, 2 * 32 * 32 * 16),
                                   ("bf16_zeros", 0, zeros, 2 * 32 * 32 * 16),
+                                  ("bf16_16x16x32_random", 2, src_bf16, 2 * 16 * 16 * 32),
+                                  ("bf16_16x16x32_chains_random", 3, src_bf16, 2 * 16 * 16 * 32),
                                   ("fp8_random", 1, src_fp8, 2 * 32 * 32 * 64),
                                   ("fp8_zeros", 1, zeros, 2 * 32 * 32 * 64)):
         def launch(iters):
@@ -482,7 +485,8 @@ def mfma_ceiling(dev, props, launch_ms=100.0, timed=5):
             evs.append(a.elapsed_time(b))
         ms = float(np.median(evs))
         flops = n_blocks * 4 * 16 * iters * flop
-        mhz, n = sustained_clock(lambda: launch(iters // 10 or 1), 1.5)
+        mhz, n = (sustained_clock(lambda: launch(iters // 10 or 1), clock_s) if clock_s > 0
+                  else (None, 0))
         res[name] = {"tflops": round(flops / ms / 1e9, 1), "launch_ms": round(ms, 3),
                      "iters": iters, "sustained_sclk_mhz": mhz, "sclk_samples": n}
         log(f"mfma ceiling {name}: {res[name]['tflops']} TFLOP/s ({ms:.3f} ms per launch of "
