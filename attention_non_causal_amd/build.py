@@ -6,7 +6,8 @@ into attention_non_causal_amd/libditattn.so.  Run as a module or call build().
 build(debug_barriers=True) builds the race-check variant libditattn_debugsync.so
 from the same sources with -DDIT_DEBUG_BARRIERS (see debug_sync in
 csrc/common.hpp); only tests load it.  build_probe() builds libditprobe.so, the
-matrix-core throughput probe `bench.py --mfma-ceiling` runs (probe/).
+matrix-core throughput and vector-issue probes that `bench.py --mfma-ceiling`
+and `bench.py --valu-issue` run (probe/).
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ LIB_NAME = "libditattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 DEBUG_BUILD_DIR = os.path.join(ROOT, "_build", "ditattn_debugsync")
 DEBUG_LIB_PATH = os.path.join(PKG, "libditattn_debugsync.so")
-PROBE_SRC = os.path.join(PKG, "probe", "mfma_ceiling.hip")
+PROBE_SRCS = [os.path.join(PKG, "probe", f) for f in ("mfma_ceiling.hip", "valu_issue.hip")]
 PROBE_LIB_PATH = os.path.join(PKG, "libditprobe.so")
 ARCH = "gfx950"
 
@@ -96,7 +97,7 @@ def build(verbose: bool = False, debug_barriers: bool = False) -> str:
 
 def build_probe(verbose: bool = False) -> str:
     tmp = PROBE_LIB_PATH + ".tmp"
-    cmd = [hipcc()] + COMMON_FLAGS + ["-shared", PROBE_SRC, "-o", tmp]
+    cmd = [hipcc()] + COMMON_FLAGS + ["-shared"] + PROBE_SRCS + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -325,6 +325,11 @@ def main():
                     help="instead of the benchmark: the dense matrix-core throughput this GPU "
                          "sustains (bf16 and e4m3, random and all-zero operands; "
                          "libditprobe.so) and its shader clock meanwhile; one JSON line")
+    ap.add_argument("--valu-issue", action="store_true",
+                    help="instead of the benchmark: shader-clock cycles per wave64 vector "
+                         "instruction of the softmax's kinds (exponential, FMA, addition, "
+                         "bf16 and e4m3 packs) at one and two waves per SIMD "
+                         "(libditprobe.so); one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device-to-device copy of 1 GiB, whose HBM "
                          "counters calibrate FETCH_SIZE / WRITE_SIZE in a --pmc profile")
@@ -343,6 +348,9 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     if args.mfma_ceiling:
         print(json.dumps(mfma_ceiling(dev, props, clock_s=args.clock_seconds)), flush=True)
+        return
+    if args.valu_issue:
+        print(json.dumps(valu_issue(dev, props)), flush=True)
         return
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -494,6 +502,47 @@ def mfma_ceiling(dev, props, launch_ms=100.0, timed=5, clock_s=1.5):
     return {"mfma_ceiling": res, "device": {"name": props.name,
                                             "arch": getattr(props, "gcnArchName", None),
                                             "cus": props.multi_processor_count}}
+
+
+def valu_issue(dev, props, iters=512):
+    """Cycles a SIMD spends per wave64 vector instruction, by kind, at one and
+    two waves per SIMD: the probe kernel (attention_non_causal_amd/probe/
+    valu_issue.hip) runs `iters` turns of 16 independent instructions per wave
+    and times them with s_memtime; the figure is the median wave's cycles /
+    (instructions per wave x waves per SIMD).  One warm launch per case, then
+    the measured one."""
+    import ctypes
+    import numpy as np
+    import torch
+    from attention_non_causal_amd import build as libbuild
+    if not os.path.exists(libbuild.PROBE_LIB_PATH):
+        raise SystemExit(f"{libbuild.PROBE_LIB_PATH} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(libbuild.PROBE_LIB_PATH)
+    lib.dit_probe_valu_issue.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.dit_probe_valu_issue.restype = ctypes.c_int
+    n_blocks = props.multi_processor_count
+    out = torch.zeros(n_blocks * 8, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"n_blocks": n_blocks, "instructions_per_wave": 16 * iters,
+           "unit": "shader-clock cycles per wave64 instruction per SIMD"}
+    for name, kind in (("v_exp_f32", 0), ("v_fma_f32", 1), ("v_add_f32", 2),
+                       ("v_cvt_pk_bf16_f32", 3), ("v_cvt_pk_fp8_f32", 4),
+                       ("v_exp_f32+v_fma_f32 alternating", 5)):
+        res[name] = {}
+        for waves in (4, 8):
+            for _ in range(2):
+                st = lib.dit_probe_valu_issue(out.data_ptr(), n_blocks, waves, iters, kind, stream)
+                assert st == 0, f"probe launch failed: HIP status {st}"
+            torch.cuda.synchronize()
+            cyc = out[: n_blocks * waves].cpu().numpy()
+            per_simd = waves // 4
+            res[name][f"{per_simd}_wave_per_simd"] = round(
+                float(np.median(cyc)) / (16 * iters * per_simd), 2)
+        log(f"valu issue {name}: {res[name]}")
+    return {"valu_issue": res, "device": {"name": props.name,
+                                          "arch": getattr(props, "gcnArchName", None),
+                                          "cus": props.multi_processor_count}}
 
 
 def run_extras(dev, steps, warmup, settle_s):

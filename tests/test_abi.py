@@ -38,7 +38,7 @@ def test_library_exports_header_functions():
 
 def test_side_libraries_export_the_same_interface():
     """The race-check build exports what the header declares, like the
-    library; the matrix-core probe exports its one entry."""
+    library; the probe library exports its two entries."""
     from attention_non_causal_amd import build as libbuild
 
     def exported(path):
@@ -46,7 +46,7 @@ def test_side_libraries_export_the_same_interface():
                              text=True, check=True).stdout
         return {line.split()[-1] for line in out.splitlines() if " T " in line}
     assert set(_lib.header_functions()) <= exported(_lib.DEBUG_LIB_PATH)
-    assert "dit_probe_mfma_ceiling" in exported(libbuild.PROBE_LIB_PATH)
+    assert {"dit_probe_mfma_ceiling", "dit_probe_valu_issue"} <= exported(libbuild.PROBE_LIB_PATH)
 
 
 def test_version_and_status_strings():

@@ -1,7 +1,9 @@
-"""The matrix-core probe behind `bench.py --mfma-ceiling` (libditprobe.so, not
-part of the attention library) runs on the GPU and returns finite sums: one
-short launch per instruction kind, with zero and with N(0,1) operands, where
-the zero operands must give exact zeros."""
+"""The probes behind `bench.py --mfma-ceiling` and `bench.py --valu-issue`
+(libditprobe.so, not part of the attention library) run on the GPU.  The
+matrix-core probe returns finite sums: one short launch per instruction kind,
+with zero and with N(0,1) operands, where the zero operands must give exact
+zeros.  The vector-issue probe returns one positive cycle count per wave, at
+least the instructions it issued."""
 import ctypes
 import os
 
@@ -22,6 +24,9 @@ def _probe():
     lib.dit_probe_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.dit_probe_mfma_ceiling.restype = ctypes.c_int
+    lib.dit_probe_valu_issue.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.dit_probe_valu_issue.restype = ctypes.c_int
     return lib
 
 
@@ -47,3 +52,20 @@ def test_probe_runs(kind):
     torch.cuda.synchronize()
     assert torch.isfinite(out).all() and (out != 0).any()
     assert lib.dit_probe_mfma_ceiling(None, out.data_ptr(), n_blocks, 3, kind, None) != 0
+
+
+@pytest.mark.parametrize("kind", range(6))
+@pytest.mark.parametrize("waves", [4, 8])
+def test_valu_issue_probe_runs(kind, waves):
+    lib = _probe()
+    dev = device()
+    n_blocks, iters = 8, 16
+    out = torch.zeros(n_blocks * waves, dtype=torch.int64, device=dev)
+    say(f"valu issue probe kind {kind}, {waves} waves per workgroup")
+    assert lib.dit_probe_valu_issue(out.data_ptr(), n_blocks, waves, iters, kind, None) == 0
+    torch.cuda.synchronize()
+    cyc = out.cpu().numpy()
+    # a wave issues at most one vector instruction per cycle
+    assert (cyc >= 16 * iters).all() and (cyc < 10 ** 9).all()
+    assert lib.dit_probe_valu_issue(out.data_ptr(), n_blocks, 5, iters, kind, None) != 0
+    assert lib.dit_probe_valu_issue(None, n_blocks, waves, iters, kind, None) != 0
