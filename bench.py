@@ -424,7 +424,15 @@ def main():
                    "cus": props.multi_processor_count,
                    "sustained_sclk_mhz": clock_mhz, "sclk_samples": clock_n,
                    "peak_basis": "2.5 PFLOP/s bf16 / 5.0 PFLOP/s fp8 dense at 2.4 GHz, "
-                                 "256 CUs"},
+                                 "256 CUs",
+                   # context only (roofline.frac stays against the 2.4 GHz peak): the
+                   # dense bf16 peak at the clock the part sustained under this load,
+                   # and the achieved rate's fraction of it
+                   "bf16_peak_at_sustained_sclk": (round(PEAK_BF16_TFLOPS * clock_mhz / 2400.0, 1)
+                                                   if clock_mhz else None),
+                   "frac_at_sustained_sclk": (round(achieved / (PEAK_BF16_TFLOPS * clock_mhz
+                                                                / 2400.0), 4)
+                                              if clock_mhz else None)},
         "host": host_info(),
         "extras": extras,
     }
