@@ -170,6 +170,39 @@ __device__ __forceinline__ void mfma_s2(f32x4& acc, const u32x4& a0, const u32x4
                  : "+v"(acc) : "v"(a0), "a"(b0), "v"(a1), "a"(b1));
 }
 
+// The same chains with one exponential between their two instructions: e =
+// 2^x, issued while the first instruction runs and before the second, which
+// waits for it.  x comes from an instruction one slot earlier, so the
+// exponential waits for nothing; e must not share registers with the
+// operands, which the second instruction still reads.
+__device__ __forceinline__ void mfma_o2_exp(f32x4& acc, const u32x4& a0, const u32x4& b0,
+                                            const u32x4& a1, const u32x4& b1, float& e, float x)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\t"
+                 "v_exp_f32 %1, %6\n\t"
+                 "v_mfma_f32_16x16x32_bf16 %0, %4, %5, %0"
+                 : "+a"(acc), "=&v"(e) : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(x));
+}
+
+__device__ __forceinline__ void mfma_s2_first_exp(f32x4& acc, const u32x4& a0, const u32x4& b0,
+                                                  const u32x4& a1, const u32x4& b1, float& e,
+                                                  float x)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %2, %3, 0\n\t"
+                 "v_exp_f32 %1, %6\n\t"
+                 "v_mfma_f32_16x16x32_bf16 %0, %4, %5, %0"
+                 : "=&v"(acc), "=&v"(e) : "v"(a0), "a"(b0), "v"(a1), "a"(b1), "v"(x));
+}
+
+__device__ __forceinline__ void mfma_s2_exp(f32x4& acc, const u32x4& a0, const u32x4& b0,
+                                            const u32x4& a1, const u32x4& b1, float& e, float x)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\t"
+                 "v_exp_f32 %1, %6\n\t"
+                 "v_mfma_f32_16x16x32_bf16 %0, %4, %5, %0"
+                 : "+v"(acc), "=&v"(e) : "v"(a0), "a"(b0), "v"(a1), "a"(b1), "v"(x));
+}
+
 // 16 wait states before vector code touches blocks the asm MFMAs may still be
 // writing (a 4-pass MFMA needs at most 11).
 __device__ __forceinline__ void acc_wait(f32x4& acc)
@@ -225,6 +258,7 @@ struct TileD128 {
     float lsum_max[2];       // largest lsum of the pass (checked against kWeightSumLimit)
     float m_used[2];         // reference maximum (scale*log2(e) units), fixed per pass
     float l_run[2];          // running sums over this lane's keys
+    float xw;                // argument of the next slot's exponential
     int copy_kt;             // tile of the current iteration (for copies issued in its slots)
     bool partial;            // the current tile has keys >= key_end
 
@@ -305,20 +339,30 @@ struct TileD128 {
             vgpr_wait(sacc[b]);
     }
 
-    // Softmax of the current tile, slot I: weight I of the order w = 4 b + i
-    // (register i of block b = 2 kb + qb), in place.  Its sum and bf16 pair
-    // come one slot later (fold), so that no instruction waits on an
-    // exponential of its own slot.
-    template <int P, int I>
-    __device__ __forceinline__ void softmax_part()
+    // Argument of weight J (of the order w = 4 b + i, register i of block b =
+    // 2 kb + qb) into xw: the scaled score less the reference maximum.
+    template <int J>
+    __device__ __forceinline__ void weight_arg()
     {
-        constexpr int b = I / 4, qb = b % 2, i = I % 4;
+        constexpr int b = J / 4, qb = b % 2, i = J % 4;
         use(m_used[qb]);
-        const float x = __builtin_fmaf(sacc[b][i], scale_log2, -m_used[qb]);
-        use(x);
-        const float e = exp2_fast(x);
+        xw = __builtin_fmaf(sacc[b][i], scale_log2, -m_used[qb]);
+        use(xw);
+    }
+
+    // Softmax of the current tile after the matrix instructions of slot I,
+    // whose asm statement computed e = 2^xw, weight I: the weight goes back
+    // into its S^T register, the argument of weight I+1 is computed for the
+    // next slot, and weight I-1 is folded (its sum and bf16 pair come one slot
+    // after its exponential, so that no instruction waits on it).
+    template <int P, int I>
+    __device__ __forceinline__ void softmax_part(float e)
+    {
+        constexpr int b = I / 4, i = I % 4;
         use(e);
         sacc[b][i] = e;
+        if constexpr (I + 1 < kSlots)
+            weight_arg<I + 1>();
         if constexpr (I > 0)
             fold<P, I - 1>();
     }
@@ -445,25 +489,29 @@ struct TileD128 {
             if (partial)
                 mask_block<7>();
         }
-        if constexpr (I % 8 == 2 || I % 8 == 4)
-            read_kf<R, I / 8, (I % 8) / 4>();
+        float e;  // weight I, computed inside the slot's asm statement
         if constexpr (I % 2 == 0) {
             constexpr int u = I / 2, cb = u / 2, qb = u % 2;
+            mfma_o2_exp(oacc[cb][qb], vf[cb % 2][0], pf[P ^ 1][0][qb], vf[cb % 2][1],
+                        pf[P ^ 1][1][qb], e, xw);
+            // (the reads come after the matrix instructions, which then issue
+            // without waiting behind them)
             if constexpr (qb == 0 && cb + 1 < kCB)
                 read_vf<R, cb + 1>();
             if constexpr (I == kSlots - 2)
                 read_vf<RN, 0>();
-            mfma_o2(oacc[cb][qb], vf[cb % 2][0], pf[P ^ 1][0][qb], vf[cb % 2][1], pf[P ^ 1][1][qb]);
         } else {
             // block b, half hs: slots 4b+5+2hs (mod 32)
             constexpr int b = I < 5 ? 7 : (I - 5) / 4, hs = I < 5 ? (I - 1) / 2 : ((I - 5) / 2) % 2;
             constexpr int kb = b / 2, qb = b % 2;
             if constexpr (hs == 0)
-                mfma_s2_first(sacc[b], kf[0], qf[qb][0], kf[1], qf[qb][1]);
+                mfma_s2_first_exp(sacc[b], kf[0], qf[qb][0], kf[1], qf[qb][1], e, xw);
             else
-                mfma_s2(sacc[b], kf[2], qf[qb][2], kf[3], qf[qb][3]);
+                mfma_s2_exp(sacc[b], kf[2], qf[qb][2], kf[3], qf[qb][3], e, xw);
         }
-        softmax_part<P, I>();
+        if constexpr (I % 8 == 2 || I % 8 == 4)
+            read_kf<R, I / 8, (I % 8) / 4>();
+        softmax_part<P, I>(e);
         if constexpr (I == Cfg::kCopySlotV)
             copy_tile<-1, W>(copy_kt + kHalf - 1);
         if constexpr (I == Cfg::kCopySlotK)
@@ -519,6 +567,7 @@ struct TileD128 {
             for (int b = 0; b < 7; ++b)
                 mask_one(b);
         }
+        weight_arg<0>();  // the first slot's exponential (after the masking)
         // re-pinned here, in the block of this iteration's reads, so that the
         // slot distances fold into their offset fields
         asm volatile("" : "+v"(v_reg));
